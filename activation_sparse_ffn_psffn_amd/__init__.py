@@ -1,0 +1,236 @@
+"""Python binding of libpsffn, the predictor-gated neuron-level sparse FFN for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libpsffn.so`` behind the C ABI in ``include/psffn.h``.  torch is used for device memory and the
+current stream.  There is no CPU fallback: importing this package without the built library
+raises.
+
+Calls mirror the C ABI by name:
+    workspace_bytes, workspace_init, predict, compact, sparse_ffn, profile_counts,
+    permute_hot_first, layernorm_f16, status_str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsffn.so")
+
+PSFFN_OK, PSFFN_E_INVALID_ARG, PSFFN_E_UNSUPPORTED, PSFFN_E_WORKSPACE, PSFFN_E_HIP = range(5)
+PSFFN_F32, PSFFN_F16, PSFFN_I4G128 = 0, 1, 2
+PSFFN_RELU, PSFFN_SWIGLU = 0, 1
+MAX_BATCH = 32
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libpsffn.so is not built (run: python -m activation_sparse_ffn_psffn_amd.build); "
+                      "there is no fallback implementation")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class _Predictor(ctypes.Structure):
+    _fields_ = [("d", _i), ("F", _i), ("r", _i), ("dt", _i), ("A", _vp), ("Q", _vp), ("c", _vp)]
+
+
+class _FFN(ctypes.Structure):
+    _fields_ = [("d", _i), ("F", _i), ("dt", _i), ("act", _i), ("w_up", _vp), ("w_gate", _vp), ("w_dT", _vp),
+                ("s_up", _vp), ("s_gate", _vp), ("s_dT", _vp), ("b_up", _vp), ("b_gate", _vp), ("b_down", _vp)]
+
+
+_P = ctypes.POINTER
+_lib.psffn_status_str.restype = ctypes.c_char_p
+_lib.psffn_status_str.argtypes = [_i]
+_lib.psffn_workspace_bytes.restype = _sz
+_lib.psffn_workspace_bytes.argtypes = [_P(_Predictor), _P(_FFN), _i]
+_lib.psffn_workspace_init.restype = _i
+_lib.psffn_workspace_init.argtypes = [_vp, _sz, _vp]
+_lib.psffn_predict.restype = _i
+_lib.psffn_predict.argtypes = [_P(_Predictor), _vp, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.psffn_compact.restype = _i
+_lib.psffn_compact.argtypes = [_vp, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]
+_lib.psffn_sparse_ffn.restype = _i
+_lib.psffn_sparse_ffn.argtypes = [_P(_FFN), _vp, _i, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.psffn_profile_counts.restype = _i
+_lib.psffn_profile_counts.argtypes = [_P(_FFN), _vp, _i, _vp, _vp]
+_lib.psffn_permute_hot_first.restype = _i
+_lib.psffn_permute_hot_first.argtypes = [_vp, _i, _vp, _P(_FFN), _P(_FFN), _P(_Predictor), _P(_Predictor), _vp, _sz,
+                                         _vp]
+_lib.psffn_layernorm_f16.restype = _i
+_lib.psffn_layernorm_f16.argtypes = [_vp, _i, _i, _f, _vp, _vp]
+
+EXPORTED = ("psffn_status_str", "psffn_workspace_bytes", "psffn_workspace_init", "psffn_predict", "psffn_compact",
+            "psffn_sparse_ffn", "psffn_profile_counts", "psffn_permute_hot_first", "psffn_layernorm_f16")
+
+
+class PsffnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (status %d)" % (where, status_str(status), status))
+
+
+def status_str(status: int) -> str:
+    return _lib.psffn_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != PSFFN_OK:
+        raise PsffnError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(t: torch.Tensor) -> int:
+    return {torch.float32: PSFFN_F32, torch.float16: PSFFN_F16, torch.uint8: PSFFN_I4G128}[t.dtype]
+
+
+@dataclass
+class Predictor:
+    """Low-rank predictor of one layer: A [r][d], Q [F][r] (fp32 or fp16, same type), c [F] fp32."""
+    A: torch.Tensor
+    Q: torch.Tensor
+    c: torch.Tensor
+
+    def struct(self) -> _Predictor:
+        r, d = self.A.shape
+        return _Predictor(d, self.Q.shape[0], r, _dt(self.A), self.A.data_ptr(), self.Q.data_ptr(),
+                          self.c.data_ptr())
+
+
+@dataclass
+class FFN:
+    """FFN weights of one layer, neuron-major.  Dense: w_* [F][d] fp32/fp16.  4-bit: w_* uint8
+    [F][d/2] with s_* fp16 [F][d/128].  Biases fp32 or None."""
+    act: str
+    w_up: torch.Tensor
+    w_dT: torch.Tensor
+    w_gate: Optional[torch.Tensor] = None
+    s_up: Optional[torch.Tensor] = None
+    s_gate: Optional[torch.Tensor] = None
+    s_dT: Optional[torch.Tensor] = None
+    b_up: Optional[torch.Tensor] = None
+    b_gate: Optional[torch.Tensor] = None
+    b_down: Optional[torch.Tensor] = None
+
+    @property
+    def d(self) -> int:
+        return self.w_up.shape[1] * (2 if self.w_up.dtype == torch.uint8 else 1)
+
+    @property
+    def F(self) -> int:
+        return self.w_up.shape[0]
+
+    def struct(self) -> _FFN:
+        p = lambda t: None if t is None else t.data_ptr()
+        return _FFN(self.d, self.F, _dt(self.w_up), PSFFN_SWIGLU if self.act == "swiglu" else PSFFN_RELU,
+                    p(self.w_up), p(self.w_gate), p(self.w_dT), p(self.s_up), p(self.s_gate), p(self.s_dT),
+                    p(self.b_up), p(self.b_gate), p(self.b_down))
+
+    def empty_like(self) -> "FFN":
+        e = lambda t: None if t is None else torch.empty_like(t)
+        return replace(self, w_up=e(self.w_up), w_dT=e(self.w_dT), w_gate=e(self.w_gate), s_up=e(self.s_up),
+                       s_gate=e(self.s_gate), s_dT=e(self.s_dT), b_up=e(self.b_up), b_gate=e(self.b_gate))
+
+
+def workspace_bytes(P: Optional[Predictor], W: Optional[FFN], B: int) -> int:
+    ps = ctypes.byref(P.struct()) if P is not None else None
+    ws = ctypes.byref(W.struct()) if W is not None else None
+    n = _lib.psffn_workspace_bytes(ps, ws, int(B))
+    if n == 0:
+        raise PsffnError(PSFFN_E_INVALID_ARG, "workspace_bytes")
+    return n
+
+
+def workspace_init(ws: torch.Tensor, stream=None):
+    _check(_lib.psffn_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "workspace_init")
+
+
+def new_workspace(P: Optional[Predictor], W: Optional[FFN], B: int, device="cuda", stream=None) -> torch.Tensor:
+    n = (workspace_bytes(P, W, B) + 255) // 256 * 256
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    workspace_init(ws, stream)
+    return ws
+
+
+def predict(P: Predictor, x: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, idx: torch.Tensor = None,
+            count: torch.Tensor = None, logits: torch.Tensor = None, stream=None):
+    """Active neurons of the batch x [B][d]: (idx int32 [F] ascending, count int32 [1]) on the device."""
+    B = x.shape[0]
+    F = P.Q.shape[0]
+    if idx is None:
+        idx = torch.empty(F, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    s = P.struct()
+    _check(_lib.psffn_predict(ctypes.byref(s), _ptr(x), B, float(thr), _ptr(idx), _ptr(count), _ptr(logits), _ptr(ws),
+                              ws.numel(), _stream(stream)), "predict")
+    return idx, count
+
+
+def compact(logits: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, idx=None, count=None, stream=None):
+    B, F = logits.shape
+    if idx is None:
+        idx = torch.empty(F, dtype=torch.int32, device=logits.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=logits.device)
+    _check(_lib.psffn_compact(_ptr(logits), B, F, float(thr), _ptr(idx), _ptr(count), _ptr(ws), ws.numel(),
+                              _stream(stream)), "compact")
+    return idx, count
+
+
+def sparse_ffn(W: FFN, x: torch.Tensor, idx: torch.Tensor, count: torch.Tensor, ws: torch.Tensor,
+               y: torch.Tensor = None, accumulate: bool = False, stream=None) -> torch.Tensor:
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty(B, W.d, dtype=torch.float32, device=x.device)
+    s = W.struct()
+    _check(_lib.psffn_sparse_ffn(ctypes.byref(s), _ptr(x), B, _ptr(idx), _ptr(count), _ptr(y), int(bool(accumulate)),
+                                 _ptr(ws), ws.numel(), _stream(stream)), "sparse_ffn")
+    return y
+
+
+def profile_counts(W: FFN, X: torch.Tensor, counts: torch.Tensor = None, stream=None) -> torch.Tensor:
+    if counts is None:
+        counts = torch.empty(W.F, dtype=torch.int32, device=X.device)
+    s = W.struct()
+    _check(_lib.psffn_profile_counts(ctypes.byref(s), _ptr(X), X.shape[0], _ptr(counts), _stream(stream)),
+           "profile_counts")
+    return counts
+
+
+def permute_hot_first(counts: torch.Tensor, W: Optional[FFN] = None, P: Optional[Predictor] = None,
+                      ws: torch.Tensor = None, stream=None):
+    """Returns (perm, W', P'): W' and P' are new buffers holding the hot-first reordering."""
+    F = counts.shape[0]
+    perm = torch.empty(F, dtype=torch.int32, device=counts.device)
+    Wd = W.empty_like() if W is not None else None
+    Pd = Predictor(P.A, torch.empty_like(P.Q), torch.empty_like(P.c)) if P is not None else None
+    sW, dW = (W.struct(), Wd.struct()) if W is not None else (None, None)
+    sP, dP = (P.struct(), Pd.struct()) if P is not None else (None, None)
+    ref = lambda v: ctypes.byref(v) if v is not None else None
+    _check(_lib.psffn_permute_hot_first(_ptr(counts), F, _ptr(perm), ref(sW), ref(dW), ref(sP), ref(dP), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(stream)), "permute_hot_first")
+    if Wd is not None and W.b_down is not None:
+        Wd.b_down = W.b_down
+    return perm, Wd, Pd
+
+
+def layernorm_f16(x: torch.Tensor, eps: float = 1e-5, out: torch.Tensor = None, stream=None) -> torch.Tensor:
+    B, d = x.shape
+    if out is None:
+        out = torch.empty(B, d, dtype=torch.float16, device=x.device)
+    _check(_lib.psffn_layernorm_f16(_ptr(x), B, d, float(eps), _ptr(out), _stream(stream)), "layernorm_f16")
+    return out

@@ -1,0 +1,224 @@
+// extern "C" boundary of libpsffn: argument validation (host only, before anything is enqueued),
+// workspace layout, and dispatch to the launchers.  See include/psffn.h for the contract.
+#include <stdint.h>
+
+#include "common.h"
+
+using namespace psffn;
+
+namespace {
+
+constexpr size_t kStateBytes = 4096;  // reserved head of every workspace (kept zero between calls)
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+St st_of(psffn_dtype dt) { return dt == PSFFN_F32 ? St::F32 : (dt == PSFFN_F16 ? St::F16 : St::I4); }
+
+size_t elem_row_bytes(psffn_dtype dt, int n) {
+  return dt == PSFFN_F32 ? (size_t)n * 4 : (dt == PSFFN_F16 ? (size_t)n * 2 : (size_t)n / 2);
+}
+
+bool batch_ok(int B) { return B >= 1 && B <= PSFFN_MAX_BATCH; }
+
+psffn_status check_pred(const psffn_predictor* P) {
+  if (!P) return PSFFN_E_INVALID_ARG;
+  if (P->d <= 0 || P->F <= 0 || P->r <= 0) return PSFFN_E_INVALID_ARG;
+  if (P->dt != PSFFN_F32 && P->dt != PSFFN_F16) return PSFFN_E_UNSUPPORTED;
+  if (P->d % 8 != 0 || P->r % 8 != 0) return PSFFN_E_UNSUPPORTED;
+  if (!P->A || !P->Q || !P->c) return PSFFN_E_INVALID_ARG;
+  if (!aligned(P->A, 16) || !aligned(P->Q, 16) || !aligned(P->c, 4)) return PSFFN_E_INVALID_ARG;
+  return PSFFN_OK;
+}
+
+psffn_status check_ffn(const psffn_ffn* W) {
+  if (!W) return PSFFN_E_INVALID_ARG;
+  if (W->d <= 0 || W->F <= 0) return PSFFN_E_INVALID_ARG;
+  if (W->dt != PSFFN_F32 && W->dt != PSFFN_F16 && W->dt != PSFFN_I4G128) return PSFFN_E_UNSUPPORTED;
+  if (W->act != PSFFN_RELU && W->act != PSFFN_SWIGLU) return PSFFN_E_UNSUPPORTED;
+  if (W->dt == PSFFN_I4G128 ? (W->d % 128 != 0) : (W->d % 8 != 0)) return PSFFN_E_UNSUPPORTED;
+  if (!W->w_up || !W->w_dT) return PSFFN_E_INVALID_ARG;
+  if (!aligned(W->w_up, 16) || !aligned(W->w_dT, 16)) return PSFFN_E_INVALID_ARG;
+  if (W->act == PSFFN_SWIGLU && (!W->w_gate || !aligned(W->w_gate, 16))) return PSFFN_E_INVALID_ARG;
+  if (W->dt == PSFFN_I4G128) {
+    if (!W->s_up || !W->s_dT || !aligned(W->s_up, 2) || !aligned(W->s_dT, 2)) return PSFFN_E_INVALID_ARG;
+    if (W->act == PSFFN_SWIGLU && (!W->s_gate || !aligned(W->s_gate, 2))) return PSFFN_E_INVALID_ARG;
+  }
+  if ((W->b_up && !aligned(W->b_up, 4)) || (W->b_gate && !aligned(W->b_gate, 4)) ||
+      (W->b_down && !aligned(W->b_down, 4)))
+    return PSFFN_E_INVALID_ARG;
+  return PSFFN_OK;
+}
+
+// per-call scratch sizes (after the reserved state head)
+size_t predict_scratch(int B, int r, int F) { return round256((size_t)B * r * 4) + round256((size_t)F + 16); }
+size_t compact_scratch(int F) { return round256((size_t)F + 16); }
+size_t ffn_scratch(int B, int d, int F) {
+  return round256((size_t)F * B * 4) + round256((size_t)kSplitCap * B * (size_t)d * 4);
+}
+
+psffn_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || !aligned(ws, 256) || ws_bytes < kStateBytes + need) return PSFFN_E_WORKSPACE;
+  return PSFFN_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+psffn_status hip_status(hipError_t e) { return e == hipSuccess ? PSFFN_OK : PSFFN_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* psffn_status_str(psffn_status s) {
+  switch (s) {
+    case PSFFN_OK: return "ok";
+    case PSFFN_E_INVALID_ARG: return "invalid argument";
+    case PSFFN_E_UNSUPPORTED: return "unsupported dtype/activation/shape combination";
+    case PSFFN_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PSFFN_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t psffn_workspace_bytes(const psffn_predictor* P, const psffn_ffn* W, int B) {
+  if (!batch_ok(B) || (!P && !W)) return 0;
+  if (P && check_pred(P) != PSFFN_OK) return 0;
+  if (W && check_ffn(W) != PSFFN_OK) return 0;
+  size_t need = 0;
+  if (P) {
+    size_t v = predict_scratch(B, P->r, P->F);
+    need = v > need ? v : need;
+  }
+  if (W) {
+    size_t v = ffn_scratch(B, W->d, W->F);
+    need = v > need ? v : need;
+    v = compact_scratch(W->F);
+    need = v > need ? v : need;
+  }
+  return kStateBytes + need;
+}
+
+psffn_status psffn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!ws || !aligned(ws, 256) || ws_bytes == 0 || ws_bytes % 16 != 0) return PSFFN_E_WORKSPACE;
+  return hip_status(launch_fill_zero(ws, ws_bytes, stream));
+}
+
+psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float logit_thr, int32_t* idx,
+                           int32_t* count, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  psffn_status st = check_pred(P);
+  if (st != PSFFN_OK) return st;
+  if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) ||
+      (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
+    return PSFFN_E_INVALID_ARG;
+  st = check_ws(ws, ws_bytes, predict_scratch(B, P->r, P->F));
+  if (st != PSFFN_OK) return st;
+  char* base = static_cast<char*>(ws) + kStateBytes;
+  float* h = reinterpret_cast<float*>(base);
+  uint8_t* flags = reinterpret_cast<uint8_t*>(base + round256((size_t)B * P->r * 4));
+  const St pt = st_of(P->dt);
+  hipError_t e = launch_pred_h(pt, P->A, x, B, P->d, P->r, h, stream);
+  if (e == hipSuccess) e = launch_pred_logits(pt, P->Q, P->c, h, B, P->r, P->F, logit_thr, logits, flags, stream);
+  if (e == hipSuccess) e = launch_scatter(flags, P->F, idx, count, stream);
+  return hip_status(e);
+}
+
+psffn_status psffn_compact(const float* logits, int B, int F, float logit_thr, int32_t* idx, int32_t* count,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!batch_ok(B) || F <= 0 || !logits || !aligned(logits, 4) || !idx || !aligned(idx, 4) || !count ||
+      !aligned(count, 4) || logit_thr != logit_thr)
+    return PSFFN_E_INVALID_ARG;
+  psffn_status st = check_ws(ws, ws_bytes, compact_scratch(F));
+  if (st != PSFFN_OK) return st;
+  uint8_t* flags = static_cast<uint8_t*>(ws) + kStateBytes;
+  hipError_t e = launch_flags_from_logits(logits, B, F, logit_thr, flags, stream);
+  if (e == hipSuccess) e = launch_scatter(flags, F, idx, count, stream);
+  return hip_status(e);
+}
+
+psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const int32_t* idx, const int32_t* count,
+                              float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream) {
+  psffn_status st = check_ffn(W);
+  if (st != PSFFN_OK) return st;
+  if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
+      !aligned(y, 4))
+    return PSFFN_E_INVALID_ARG;
+  st = check_ws(ws, ws_bytes, ffn_scratch(B, W->d, W->F));
+  if (st != PSFFN_OK) return st;
+  char* base = static_cast<char*>(ws) + kStateBytes;
+  float* a = reinterpret_cast<float*>(base);
+  float* part = reinterpret_cast<float*>(base + round256((size_t)W->F * B * 4));
+  const St wt = st_of(W->dt);
+  hipError_t e = launch_up(wt, W->act, *W, x, B, idx, count, a, stream);
+  if (e == hipSuccess) e = launch_down(wt, *W, a, B, idx, count, part, stream);
+  if (e == hipSuccess) e = launch_reduce(part, count, W->F, B, W->d, W->b_down, y, accumulate, stream);
+  return hip_status(e);
+}
+
+psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int32_t* counts, hipStream_t stream) {
+  psffn_status st = check_ffn(W);
+  if (st != PSFFN_OK) return st;
+  if (T < 1 || !X || !aligned(X, 16) || !counts || !aligned(counts, 4)) return PSFFN_E_INVALID_ARG;
+  return hip_status(launch_profile_counts(st_of(W->dt), *W, X, T, counts, stream));
+}
+
+psffn_status psffn_permute_hot_first(const int32_t* counts, int F, int32_t* perm, const psffn_ffn* src,
+                                     const psffn_ffn* dst, const psffn_predictor* psrc, const psffn_predictor* pdst,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (F <= 0 || !counts || !aligned(counts, 4) || !perm || !aligned(perm, 4)) return PSFFN_E_INVALID_ARG;
+  if ((src == nullptr) != (dst == nullptr) || (psrc == nullptr) != (pdst == nullptr)) return PSFFN_E_INVALID_ARG;
+  struct Job {
+    const void* s;
+    void* t;
+    size_t rb;
+  } jobs[12];
+  int nj = 0;
+  auto add = [&](const void* s, const void* t, size_t rb) -> bool {
+    if (!s && !t) return true;
+    if (!s || !t) return false;
+    if (overlaps(s, rb * F, t, rb * F)) return false;
+    jobs[nj++] = Job{s, const_cast<void*>(t), rb};
+    return true;
+  };
+  if (src) {
+    psffn_status st = check_ffn(src);
+    if (st == PSFFN_OK) st = check_ffn(dst);
+    if (st != PSFFN_OK) return st;
+    if (src->F != F || dst->F != F || src->d != dst->d || src->dt != dst->dt || src->act != dst->act)
+      return PSFFN_E_INVALID_ARG;
+    const size_t rb = elem_row_bytes(src->dt, src->d);
+    const size_t sb = src->dt == PSFFN_I4G128 ? (size_t)(src->d / 128) * 2 : 0;
+    bool ok = add(src->w_up, dst->w_up, rb) && add(src->w_dT, dst->w_dT, rb) &&
+              (src->act != PSFFN_SWIGLU || add(src->w_gate, dst->w_gate, rb)) &&
+              add(src->b_up, dst->b_up, 4) && add(src->b_gate, dst->b_gate, 4);
+    if (ok && sb) {
+      ok = add(src->s_up, dst->s_up, sb) && add(src->s_dT, dst->s_dT, sb) &&
+           (src->act != PSFFN_SWIGLU || add(src->s_gate, dst->s_gate, sb));
+    }
+    if (!ok) return PSFFN_E_INVALID_ARG;
+  }
+  if (psrc) {
+    psffn_status st = check_pred(psrc);
+    if (st == PSFFN_OK) st = check_pred(pdst);
+    if (st != PSFFN_OK) return st;
+    if (psrc->F != F || pdst->F != F || psrc->r != pdst->r || psrc->d != pdst->d || psrc->dt != pdst->dt)
+      return PSFFN_E_INVALID_ARG;
+    if (!add(psrc->Q, pdst->Q, elem_row_bytes(psrc->dt, psrc->r)) || !add(psrc->c, pdst->c, 4))
+      return PSFFN_E_INVALID_ARG;
+  }
+  hipError_t e = launch_hot_first_perm(counts, F, perm, stream);
+  for (int j = 0; j < nj && e == hipSuccess; ++j) e = launch_gather_rows(jobs[j].s, jobs[j].t, perm, F, jobs[j].rb, stream);
+  return hip_status(e);
+}
+
+psffn_status psffn_layernorm_f16(const float* x, int B, int d, float eps, void* out_f16, hipStream_t stream) {
+  if (B < 1 || d < 1 || !x || !aligned(x, 4) || !out_f16 || !aligned(out_f16, 2) || !(eps >= 0.f))
+    return PSFFN_E_INVALID_ARG;
+  return hip_status(launch_layernorm_f16(x, B, d, eps, out_f16, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// Internal definitions of libpsffn (gfx950 / CDNA4, wave64): storage traits, 16-byte lane
+// vectors, dot products, wave reductions, workspace layout and the launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/psffn.h"
+
+namespace psffn {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;  // 4 waves per workgroup
+constexpr int kSplitCap = 64;  // max number of k-splits of the down projection (partials buffer)
+constexpr int kSplitMinRows = 16;  // min rows per k-split
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+enum class St : int { F32 = 0, F16 = 1, I4 = 2 };
+
+// ----------------------------------------------------------------------------------------
+// elementwise helpers
+
+__device__ __forceinline__ float wave_sum(float v) {
+  // xor butterfly: every lane ends with the same, order-fixed sum
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_lane() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+
+// 8 fp16 weights x 8 fp16 activations, fp32 accumulation (products of two halves are exact in fp32)
+__device__ __forceinline__ float dot8_f16(uint4 w, uint4 x, float acc) {
+  acc = dot2_f16(w.x, x.x, acc);
+  acc = dot2_f16(w.y, x.y, acc);
+  acc = dot2_f16(w.z, x.z, acc);
+  acc = dot2_f16(w.w, x.w, acc);
+  return acc;
+}
+
+__device__ __forceinline__ float dot4_f32(uint4 w, uint4 x, float acc) {
+  acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+  acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+  acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+  acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+  return acc;
+}
+
+// 8 fp16 weights x 8 fp32 values (the predictor's second stage keeps h in fp32)
+__device__ __forceinline__ float dot8_f16_f32(uint4 w, float4 h0, float4 h1, float acc) {
+  acc = fmaf(h2f(w.x & 0xffff), h0.x, acc);
+  acc = fmaf(h2f(w.x >> 16), h0.y, acc);
+  acc = fmaf(h2f(w.y & 0xffff), h0.z, acc);
+  acc = fmaf(h2f(w.y >> 16), h0.w, acc);
+  acc = fmaf(h2f(w.z & 0xffff), h1.x, acc);
+  acc = fmaf(h2f(w.z >> 16), h1.y, acc);
+  acc = fmaf(h2f(w.w & 0xffff), h1.z, acc);
+  acc = fmaf(h2f(w.w >> 16), h1.w, acc);
+  return acc;
+}
+
+// ---- 4-bit weights.  One 32-bit word holds 8 consecutive elements e0..e7, e_k in bits
+// [4k, 4k+4), each a two's-complement nibble.  Decoding trick: (nibble ^ 8) placed in the
+// mantissa of the fp16 1024.0 gives 1024 + q + 8 exactly; subtracting 1032 leaves q exactly.
+// The pairs come out as (e0,e4), (e1,e5), (e2,e6), (e3,e7); activations are paired the same
+// way by pair_x8.
+__device__ __forceinline__ half2_t i4_pair(uint32_t w, int shift) {
+  uint32_t b = ((w >> shift) & 0x000F000Fu) ^ 0x64086408u;
+  half2_t v = __builtin_bit_cast(half2_t, b);
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  return v - off;
+}
+
+// 8 fp16 activations x0..x7 -> pairs (x0,x4), (x1,x5), (x2,x6), (x3,x7)
+__device__ __forceinline__ uint4 pair_x8(uint4 x) {
+  uint4 p;
+  p.x = (x.x & 0xffffu) | (x.z << 16);
+  p.y = (x.x >> 16) | (x.z & 0xffff0000u);
+  p.z = (x.y & 0xffffu) | (x.w << 16);
+  p.w = (x.y >> 16) | (x.w & 0xffff0000u);
+  return p;
+}
+
+// sum_{k<8} q_k * x_k for one word of nibbles and paired activations (exact products)
+__device__ __forceinline__ float dot8_i4(uint32_t w, uint4 px, float acc) {
+  acc = __builtin_amdgcn_fdot2(i4_pair(w, 0), __builtin_bit_cast(half2_t, px.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(i4_pair(w, 4), __builtin_bit_cast(half2_t, px.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(i4_pair(w, 8), __builtin_bit_cast(half2_t, px.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(i4_pair(w, 12), __builtin_bit_cast(half2_t, px.w), acc, false);
+  return acc;
+}
+
+// signed nibble k (0..7) of a word as float
+__device__ __forceinline__ float i4_elem(uint32_t w, int k) {
+  return (float)(((int32_t)(w << (28 - 4 * k))) >> 28);
+}
+
+// ----------------------------------------------------------------------------------------
+// workspace layout (bytes, every region 256-byte aligned)
+
+struct WsLayout {
+  size_t h = 0, flags = 0, act = 0, part = 0, total = 0;
+};
+
+__host__ __device__ inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(int d_pred, int r, int F, int d_ffn, int B) {
+  WsLayout L;
+  size_t off = 0;
+  L.h = off;
+  off += round256((size_t)B * (size_t)(r > 0 ? r : 0) * sizeof(float));
+  L.flags = off;
+  off += round256((size_t)(F > 0 ? F : 0) + 16);
+  L.act = off;
+  off += round256((size_t)(F > 0 ? F : 0) * (size_t)B * sizeof(float));
+  L.part = off;
+  off += round256((size_t)kSplitCap * (size_t)B * (size_t)(d_ffn > 0 ? d_ffn : 0) * sizeof(float));
+  L.total = off;
+  (void)d_pred;
+  return L;
+}
+
+// ----------------------------------------------------------------------------------------
+// launchers (return hipSuccess or the launch error)
+
+hipError_t launch_pred_h(St st, const void* A, const void* x, int B, int d, int r, float* h, hipStream_t s);
+hipError_t launch_pred_logits(St st, const void* Q, const float* c, const float* h, int B, int r, int F, float thr,
+                              float* logits, uint8_t* flags, hipStream_t s);
+hipError_t launch_flags_from_logits(const float* logits, int B, int F, float thr, uint8_t* flags, hipStream_t s);
+hipError_t launch_scatter(const uint8_t* flags, int F, int32_t* idx, int32_t* count, hipStream_t s);
+hipError_t launch_up(St st, psffn_act act, const psffn_ffn& W, const void* x, int B, const int32_t* idx,
+                     const int32_t* count, float* a, hipStream_t s);
+hipError_t launch_down(St st, const psffn_ffn& W, const float* a, int B, const int32_t* idx, const int32_t* count,
+                       float* part, hipStream_t s);
+hipError_t launch_reduce(const float* part, const int32_t* count, int F, int B, int d, const float* b_down, float* y,
+                         int accumulate, hipStream_t s);
+hipError_t launch_profile_counts(St st, const psffn_ffn& W, const void* X, int T, int32_t* counts, hipStream_t s);
+hipError_t launch_hot_first_perm(const int32_t* counts, int F, int32_t* perm, hipStream_t s);
+hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* perm, int F, size_t row_bytes,
+                              hipStream_t s);
+hipError_t launch_layernorm_f16(const float* x, int B, int d, float eps, void* out, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace psffn
+
+namespace psffn {
+
+// ----------------------------------------------------------------------------------------
+// One lane's 16-byte slice of a weight row against the matching activations of one token.
+//   F32: 4 elements, F16: 8 elements, I4: 32 elements (4 words of nibbles, one group scale).
+// `e` is the element index of the slice's first element; x points at the token's row.
+
+template <St WT> struct Tr;
+template <> struct Tr<St::F32> { static constexpr int EPL = 4; static constexpr int ESZ = 4; };
+template <> struct Tr<St::F16> { static constexpr int EPL = 8; static constexpr int ESZ = 2; };
+template <> struct Tr<St::I4> { static constexpr int EPL = 32; static constexpr int ESZ = 0; };
+
+// bytes of one weight row of d elements
+template <St WT> __host__ __device__ inline size_t row_bytes(int d) {
+  return WT == St::F32 ? (size_t)d * 4 : (WT == St::F16 ? (size_t)d * 2 : (size_t)d / 2);
+}
+
+template <St WT>
+__device__ __forceinline__ float dot16(uint4 w, const void* __restrict__ x, int e, float scale, float acc) {
+  if constexpr (WT == St::F32) {
+    uint4 xv = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(x) + e);
+    return dot4_f32(w, xv, acc);
+  } else if constexpr (WT == St::F16) {
+    uint4 xv = *reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(x) + e);
+    return dot8_f16(w, xv, acc);
+  } else {
+    const uint4* xp = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(x) + e);
+    float part = 0.f;
+    part = dot8_i4(w.x, pair_x8(xp[0]), part);
+    part = dot8_i4(w.y, pair_x8(xp[1]), part);
+    part = dot8_i4(w.z, pair_x8(xp[2]), part);
+    part = dot8_i4(w.w, pair_x8(xp[3]), part);
+    return fmaf(scale, part, acc);
+  }
+}
+
+}  // namespace psffn

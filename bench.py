@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
+
+A step is one decode token through one FFN layer: predict (h = A x, logits, threshold,
+compaction) then the sparse FFN over the predicted neurons.  The default workload is the
+OPT-30B-shaped ReLU layer: d = 7168, F = 28672, predictor rank 1024, fp16 weights with fp32
+accumulation, batch 1, Zipf(1.1) firing at mean density 0.03, neurons permuted hot-first by a
+512-token profile.  Weights are random (synthetic); inputs are resident in HBM before timing.
+
+To measure HBM and not the 256 MB Infinity Cache, the steps rotate over `--copies` independent
+copies of the layer (8 copies: ~7 GB, the predictor alone 590 MB), as a decode through a deep
+layer stack would.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN µs/layer and achieved HBM GB/s (% of roofline) at batch 1"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(spec, B, n_active):
+    """Bytes the method must move for one step with n_active listed neurons (per-step mean)."""
+    e_p = 4 if spec.storage == "f32" else 2
+    e_x = 4 if spec.storage == "f32" else 2
+    d, F, r = spec.d, spec.F, spec.r
+    pred = (r * d + F * r) * e_p + 4 * F + B * d * e_x
+    if spec.storage == "i4":
+        rowb = d // 2 + 2 * (d // 128)
+    else:
+        rowb = d * e_x
+    m = 3 if spec.act == "swiglu" else 2
+    rows = m * n_active * rowb + 4 * n_active
+    out = B * d * 4
+    return pred, rows + out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--copies", type=int, default=8)
+    ap.add_argument("--workload", default="opt30b_relu_f16")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--no-events", action="store_true", help="time only the whole region (no per-call events)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py: this build measures one GPU only (the path is a single-GPU decode step); "
+            "--gpus %d is not supported" % args.gpus)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import activation_sparse_ffn_psffn_amd as ps
+    import synth
+
+    spec = synth.CONFIGS[args.workload]
+    B = args.batch
+    dev = "cuda"
+    torch.cuda.init()
+    log("workload", spec.name, "B", B)
+    t0 = time.time()
+    L = synth.make_layer(spec, seed=0, device=dev)
+    W = ps.FFN(spec.act, L.w_up, L.w_dT, w_gate=L.w_gate, s_up=L.s_up, s_gate=L.s_gate, s_dT=L.s_dT, b_up=L.b_up,
+               b_gate=L.b_gate, b_down=L.b_down)
+    P = ps.Predictor(L.A, L.Q, L.c)
+    if spec.hot_first:
+        Xp = synth.make_tokens(spec, spec.profile_tokens, seed=0, stream="profile", device=dev)
+        counts = ps.profile_counts(W, Xp)
+        perm, W, P = ps.permute_hot_first(counts, W, P)
+        del Xp, L
+    torch.cuda.synchronize()
+    log("layer ready in %.1f s" % (time.time() - t0))
+
+    def clone(W, P):
+        c = lambda t: None if t is None else t.clone()
+        return (ps.FFN(W.act, c(W.w_up), c(W.w_dT), w_gate=c(W.w_gate), s_up=c(W.s_up), s_gate=c(W.s_gate),
+                       s_dT=c(W.s_dT), b_up=c(W.b_up), b_gate=c(W.b_gate), b_down=c(W.b_down)),
+                ps.Predictor(c(P.A), c(P.Q), c(P.c)))
+
+    copies = [(W, P)] + [clone(W, P) for _ in range(args.copies - 1)]
+    ntok = spec.tokens
+    X = synth.make_tokens(spec, ntok * B, seed=0, device=dev).reshape(ntok, B, spec.d)
+    ws = ps.new_workspace(P, W, B)
+    F = spec.F
+    idx = torch.empty(F, dtype=torch.int32, device=dev)
+    K, Wm = args.steps, args.warmup
+    counts_all = torch.zeros(K, dtype=torch.int32, device=dev)
+    y = torch.empty(B, spec.d, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(t, cnt, ev=None):
+        Wc, Pc = copies[t % len(copies)]
+        x = X[t % ntok]
+        if ev is not None:
+            ev[0].record(stream)
+        ps.predict(Pc, x, ws, idx=idx, count=cnt, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ps.sparse_ffn(Wc, x, idx, cnt, ws, y=y, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    scratch_cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    for t in range(Wm):
+        step(t, scratch_cnt)
+    torch.cuda.synchronize()
+
+    evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_start.record(stream)
+    for t in range(K):
+        step(Wm + t, counts_all[t:t + 1], None if evs is None else evs[t])
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e_start.elapsed_time(e_end)
+    us_per_step = total_ms * 1e3 / K
+
+    counts_np = counts_all.cpu().numpy().astype(np.float64)
+    n_mean = float(counts_np.mean())
+    pred_bytes, ffn_bytes = algorithmic_bytes(spec, B, n_mean)
+    step_bytes = pred_bytes + ffn_bytes
+    layer_gbps = step_bytes / (us_per_step * 1e-6) / 1e9
+
+    roof = None
+    breakdown = None
+    if evs is not None:
+        pred_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+        ffn_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+        breakdown = {"predict_us": round(pred_us, 3), "sparse_ffn_us": round(ffn_us, 3)}
+        achieved = pred_bytes / (pred_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "kernel": "psffn_predict (fp16 predictor stream: A then Q, threshold, compaction)",
+                "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, copies[0], X, B, args.cpu_tokens)
+
+    out = {
+        "metric": METRIC, "value": round(us_per_step, 3), "unit": "us/layer", "n_gpus": 1, "steps": K,
+        "warmup": Wm, "ms_per_step": round(total_ms / K, 6), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16" if spec.storage != "f32" else "f32", "data": "synthetic",
+        "config": {"workload": "%s: d=%d F=%d r=%d %s %s batch %d, Zipf(%.1f) density %.2f%s, %d layer copies" % (
+            spec.name, spec.d, spec.F, spec.r, spec.storage, spec.act, B, spec.zipf, spec.density,
+            ", hot-first" if spec.hot_first else "", len(copies)), "batch": B, "d": spec.d, "F": spec.F,
+            "r": spec.r},
+        "layer": {"gbps": round(layer_gbps, 1), "frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
+                  "algorithmic_bytes_per_step": int(step_bytes), "mean_active": round(n_mean, 2),
+                  "tokens_per_s": round(1e6 / us_per_step * B, 1), "breakdown": breakdown},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, copy0, X, B, ntok):
+    """The oracle (single-threaded fp64 C loops) timed on this host on `ntok` decode steps of the
+    same workload: predict, compact, sparse FFN over its own list."""
+    import numpy as np
+
+    import oracle
+
+    W, P = copy0
+    g = lambda t: None if t is None else t.detach().cpu().numpy()
+    A, Q, c = g(P.A), g(P.Q), g(P.c)
+    lay = oracle.Layer(spec.act, g(W.w_up), g(W.w_dT), w_gate=g(W.w_gate), s_up=g(W.s_up), s_gate=g(W.s_gate),
+                       s_dT=g(W.s_dT), b_up=g(W.b_up), b_gate=g(W.b_gate), b_down=g(W.b_down))
+    Xn = X[:ntok].cpu().numpy()
+    oracle.build()
+    t0 = time.perf_counter()
+    for t in range(ntok):
+        oracle.predicted_layer(A, Q, c, lay, Xn[t])
+    dt = time.perf_counter() - t0
+    log("cpu baseline: %d steps in %.2f s" % (ntok, dt))
+    return {"value": round(dt / ntok * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "sample": "%d decode steps (batch %d) of the same layer: predict, compact, sparse FFN; "
+                      "single-threaded fp64 C" % (ntok, B)}
+
+
+if __name__ == "__main__":
+    main()

@@ -72,7 +72,7 @@ def _L():
         _lib.orc_sparse_ffn.restype = None
         _lib.orc_sparse_ffn.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p, _i, _p]
         _lib.orc_fire_counts.restype = None
-        _lib.orc_fire_counts.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p]
+        _lib.orc_fire_counts.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _d, _p]
         _lib.orc_hot_first_perm.restype = None
         _lib.orc_hot_first_perm.argtypes = [_p, _i, _p]
         _lib.orc_layernorm.restype = None
@@ -224,12 +224,14 @@ class Layer:
     def dense_ffn(self, x):
         return self.sparse_ffn(x, np.arange(self.F, dtype=np.int32))
 
-    def fire_counts(self, X):
+    def fire_counts(self, X, thr: float = 0.0):
+        """counts[i] = number of tokens of X whose deciding pre-activation of neuron i exceeds thr
+        (the profile is thr = 0)."""
         X = np.ascontiguousarray(np.atleast_2d(X))
         counts = np.empty(self.F, dtype=np.int32)
         _L().orc_fire_counts(self.dt, self.act, self.d, self.F, _ptr(self.w_up), _ptr(self.s_up), _ptr(self.w_gate),
                              _ptr(self.s_gate), _ptr(self.b_up), _ptr(self.b_gate), _dense_code(X), _ptr(X),
-                             X.shape[0], _ptr(counts))
+                             X.shape[0], float(thr), _ptr(counts))
         return counts
 
     def permuted(self, perm):

@@ -189,10 +189,11 @@ void orc_sparse_ffn(int dt_w, int act, int d, int F, const void* w_up, const uin
 
 /* Offline activation profile (Summary, 2nd paragraph; Interesting ideas, I1): for each neuron,
  * the number of the T tokens for which it truly fires -- pre-activation > 0 for ReLU, gate
- * pre-activation > 0 for SwiGLU. */
+ * pre-activation > 0 for SwiGLU.  `thr` generalises the 0 (the definition is thr = 0; other
+ * values bracket a count computed in lower precision). */
 void orc_fire_counts(int dt_w, int act, int d, int F, const void* w_up, const uint16_t* s_up, const void* w_gate,
                      const uint16_t* s_gate, const float* b_up, const float* b_gate, int dt_x, const void* x, int T,
-                     int32_t* counts) {
+                     double thr, int32_t* counts) {
   const void* w = act == ORC_RELU ? w_up : w_gate;
   const uint16_t* s = act == ORC_RELU ? s_up : s_gate;
   const float* bias = act == ORC_RELU ? b_up : b_gate;
@@ -201,7 +202,7 @@ void orc_fire_counts(int dt_w, int act, int d, int F, const void* w_up, const ui
     for (int t = 0; t < T; ++t) {
       double z = bias ? (double)bias[i] : 0.0;
       for (int k = 0; k < d; ++k) z += weight_elem(dt_w, w, s, d, i, k) * dense_elem(dt_x, x, d, t, k);
-      if (z > 0.0) ++n;
+      if (z > thr) ++n;
     }
     counts[i] = n;
   }

@@ -240,3 +240,12 @@ def make_residual(spec: LayerSpec, n: int, seed: int = 0, device="cpu", d: int =
     """Initial fp32 residual stream of the decode stack, x0 ~ N(0, I)."""
     d = d or spec.d
     return torch.randn(n, d, generator=_gen(seed, 0, "x0", device), device=device, dtype=torch.float32)
+
+
+def profile_like_counts(p: np.ndarray, T: int, seed: int = 0) -> np.ndarray:
+    """Synthetic fire counts with the statistics of a T-token profile: counts_i ~ Binomial(T, p_i),
+    int32.  An input for the hot-first order that does not depend on any implementation."""
+    g = torch.Generator().manual_seed(int(seed) * 7919 + 3)
+    pt = torch.from_numpy(np.asarray(p, dtype=np.float64)).to(torch.float32)
+    c = torch.binomial(torch.full_like(pt, float(T)), pt, generator=g)
+    return c.to(torch.int32).numpy()

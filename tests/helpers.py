@@ -1,0 +1,78 @@
+"""Shared helpers of the GPU parity tests: descriptors for both sides built from one synthetic
+layer, and the comparison rules.
+
+Comparison rules (parity bar):
+  * active sets: bit-exact, except neurons whose oracle logit (max over the batch) lies within
+    BAND = 1e-6 of the threshold, where fp32 and fp64 accumulation may legitimately disagree;
+  * FFN outputs: ||y - y_ref||_inf / ||y_ref||_inf <= 1e-5 for fp32 weights, 2e-3 for fp16 and
+    4-bit weights (fp32 accumulation); y_ref == 0 requires y == 0 exactly;
+  * integer and index outputs (counts, permutation, compaction of given logits): bit-exact.
+Oracle inputs only ever come from the synthetic generator or the oracle itself.
+"""
+from dataclasses import replace
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+BAND = 1e-6
+
+
+def tol_for(storage: str) -> float:
+    return 1e-5 if storage == "f32" else 2e-3
+
+
+def ffn_of(L, ps):
+    return ps.FFN(L.spec.act, L.w_up, L.w_dT, w_gate=L.w_gate, s_up=L.s_up, s_gate=L.s_gate, s_dT=L.s_dT, b_up=L.b_up,
+                  b_gate=L.b_gate, b_down=L.b_down)
+
+
+def pred_of(L, ps):
+    return ps.Predictor(L.A, L.Q, L.c)
+
+
+def oracle_layer(n: dict, act: str, b_down=None):
+    return oracle.Layer(act, n["w_up"], n["w_dT"], w_gate=n["w_gate"], s_up=n["s_up"], s_gate=n["s_gate"],
+                        s_dT=n["s_dT"], b_up=n["b_up"], b_gate=n["b_gate"],
+                        b_down=n["b_down"] if b_down is None else b_down)
+
+
+def spec_variant(name: str, **kw):
+    return replace(synth.CONFIGS[name], **kw)
+
+
+def check_set(idx, count, logits_ref, thr=0.0):
+    """GPU list (idx tensor, count tensor) against oracle logits [B][F]; returns stats."""
+    F = logits_ref.shape[1]
+    n = int(count.cpu()[0])
+    assert 0 <= n <= F
+    got_idx = idx[:n].cpu().numpy()
+    assert np.all(np.diff(got_idx) > 0), "list not strictly ascending"
+    assert n == 0 or (got_idx[0] >= 0 and got_idx[-1] < F)
+    m = logits_ref.max(axis=0)
+    ref = m > thr
+    near = np.abs(m - thr) < BAND
+    got = np.zeros(F, dtype=bool)
+    got[got_idx] = True
+    bad = (got != ref) & ~near
+    assert not bad.any(), "active-set mismatch outside the band at neurons %s (logits %s)" % (
+        np.flatnonzero(bad)[:8], m[bad][:8])
+    return {"count": n, "ref_count": int(ref.sum()), "in_band_diff": int(((got != ref) & near).sum()),
+            "exact": bool((got == ref).all())}
+
+
+def rel_inf(y, ref) -> float:
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.abs(ref).max() if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if np.all(y == 0) else float("inf")
+    return float(np.abs(y - ref).max() / den)
+
+
+def check_y(y, ref, tol):
+    e = rel_inf(y, ref)
+    assert e <= tol, "max relative error %.3e > %.1e" % (e, tol)
+    return e

@@ -1,0 +1,224 @@
+"""GPU parity of the HIP path against the CPU oracle on small ragged shapes (several tiles plus a
+ragged tail in every dimension), every storage type and activation, batches 1..32, and the edge
+lists (empty, all neurons, unordered, perfect predictor).  Calls go through the C ABI via the
+Python binding; inputs come from the seeded generator."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import BAND, check_set, check_y, ffn_of, oracle_layer, pred_of, rel_inf, spec_variant, tol_for
+
+pytestmark = pytest.mark.gpu
+
+ps = pytest.importorskip("activation_sparse_ffn_psffn_amd")
+DEV = "cuda"
+
+# (label, base workload, overrides): d and F are not multiples of the kernels' tiles
+CASES = [
+    ("f32_relu", "tiny_relu_f32", dict(d=264, F=1000, r=40)),
+    ("f16_relu", "opt30b_relu_f16", dict(d=1288, F=2000, r=136, density=0.05)),
+    ("f16_swiglu", "llama2_13b_swiglu_f16", dict(d=1032, F=1500, r=72)),
+    ("i4_relu", "opt175b_relu_i4", dict(d=1152, F=1200, r=64, density=0.08)),
+    ("i4_swiglu", "opt175b_relu_i4", dict(d=640, F=700, r=32, act="swiglu", density=0.4)),
+    ("f32_swiglu", "tiny_relu_f32", dict(d=136, F=333, r=16, act="swiglu", density=0.3)),
+]
+
+_cache = {}
+
+
+def setup_case(label, seed=0):
+    if label in _cache:
+        return _cache[label]
+    _, base, kw = next(c for c in CASES if c[0] == label)
+    dims = {k: kw[k] for k in ("d", "F", "r")}
+    spec = spec_variant(base, **{k: v for k, v in kw.items() if k not in dims})
+    torch.cuda.synchronize()
+    L = synth.make_layer(spec, seed=seed, device=DEV, **dims)
+    n = L.numpy()
+    X = synth.make_tokens(L.spec, 40, seed=seed, device=DEV)
+    out = dict(spec=L.spec, L=L, n=n, X=X, Xn=X.cpu().numpy(), W=ffn_of(L, ps), P=pred_of(L, ps),
+               orc=oracle_layer(n, L.spec.act))
+    out["ws"] = ps.new_workspace(out["P"], out["W"], ps.MAX_BATCH)
+    _cache[label] = out
+    return out
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+@pytest.mark.parametrize("B", [1, 3, 8, 32])
+def test_predict_sets_and_logits(label, B):
+    c = setup_case(label)
+    say("predict", label, "B", B)
+    x = c["X"][:B].contiguous()
+    F = c["spec"].F
+    logits = torch.empty(B, F, dtype=torch.float32, device=DEV)
+    idx, count = ps.predict(c["P"], x, c["ws"], logits=logits)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(c["n"]["A"], c["n"]["Q"], c["n"]["c"], c["Xn"][:B])
+    st = check_set(idx, count, ref)
+    dl = np.abs(logits.cpu().numpy().astype(np.float64) - ref).max()
+    say("  count", st, "max|dlogit| %.2e" % dl)
+    assert dl < 1e-5 * (1 + np.abs(ref).max())
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+@pytest.mark.parametrize("B", [1, 2, 8, 32])
+def test_sparse_ffn_on_oracle_list(label, B):
+    c = setup_case(label)
+    say("sparse_ffn", label, "B", B)
+    x = c["X"][:B].contiguous()
+    ref_logits = oracle.predict_logits(c["n"]["A"], c["n"]["Q"], c["n"]["c"], c["Xn"][:B])
+    lst = oracle.compact(ref_logits)
+    idx = torch.from_numpy(lst).to(DEV)
+    count = torch.tensor([len(lst)], dtype=torch.int32, device=DEV)
+    y = ps.sparse_ffn(c["W"], x, idx, count, c["ws"])
+    torch.cuda.synchronize()
+    y_ref = c["orc"].sparse_ffn(c["Xn"][:B], lst)
+    e = check_y(y.cpu().numpy(), y_ref, tol_for(c["spec"].storage))
+    say("  rows", len(lst), "rel err %.2e" % e)
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+def test_edge_lists(label):
+    c = setup_case(label)
+    say("edge lists", label)
+    F, d = c["spec"].F, c["spec"].d
+    x = c["X"][:2].contiguous()
+    xn = c["Xn"][:2]
+    tol = tol_for(c["spec"].storage)
+    # empty list: y = b_down exactly (and 0 without b_down)
+    idx0 = torch.zeros(F, dtype=torch.int32, device=DEV)
+    cnt0 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y = ps.sparse_ffn(c["W"], x, idx0, cnt0, c["ws"])
+    assert torch.count_nonzero(y).item() == 0
+    bd = torch.randn(d, generator=torch.Generator().manual_seed(5)).to(DEV)
+    Wb = ps.FFN(**{**c["W"].__dict__, "b_down": bd})
+    y = ps.sparse_ffn(Wb, x, idx0, cnt0, c["ws"])
+    assert torch.equal(y, bd.expand(2, d))
+    # all neurons = dense FFN
+    alln = np.arange(F, dtype=np.int32)
+    y = ps.sparse_ffn(c["W"], x, torch.from_numpy(alln).to(DEV), torch.tensor([F], dtype=torch.int32, device=DEV),
+                      c["ws"])
+    check_y(y.cpu().numpy(), c["orc"].dense_ffn(xn), tol)
+    # any order: a shuffled subset
+    rng = np.random.default_rng(1)
+    sub = rng.permutation(F)[: F // 3].astype(np.int32)
+    y = ps.sparse_ffn(c["W"], x, torch.from_numpy(sub).to(DEV),
+                      torch.tensor([len(sub)], dtype=torch.int32, device=DEV), c["ws"])
+    check_y(y.cpu().numpy(), c["orc"].sparse_ffn(xn, sub), tol)
+    # a single neuron, with b_down
+    one = np.array([F - 1], dtype=np.int32)
+    ob = oracle_layer(c["n"], c["spec"].act, b_down=bd.cpu().numpy())
+    y = ps.sparse_ffn(Wb, x, torch.from_numpy(one).to(DEV), torch.tensor([1], dtype=torch.int32, device=DEV),
+                      c["ws"])
+    check_y(y.cpu().numpy(), ob.sparse_ffn(xn, one), tol)
+
+
+@pytest.mark.parametrize("label", ["f32_relu", "f16_relu", "i4_relu"])
+def test_perfect_predictor_list_gives_dense(label):
+    c = setup_case(label)
+    say("perfect predictor", label)
+    xn = c["Xn"][:1]
+    dense = c["orc"].dense_ffn(xn)
+    # the oracle's own firing set {z > 0}: neurons outside it contribute exactly 0 under ReLU
+    z_cnt = c["orc"].fire_counts(xn)
+    lst = np.flatnonzero(z_cnt > 0).astype(np.int32)
+    assert np.array_equal(c["orc"].sparse_ffn(xn, lst), dense)
+    y = ps.sparse_ffn(c["W"], c["X"][:1].contiguous(), torch.from_numpy(lst).to(DEV),
+                      torch.tensor([len(lst)], dtype=torch.int32, device=DEV), c["ws"])
+    check_y(y.cpu().numpy(), dense, tol_for(c["spec"].storage))
+
+
+@pytest.mark.parametrize("label", ["f16_relu", "i4_relu", "f16_swiglu"])
+def test_accumulate_and_determinism(label):
+    c = setup_case(label)
+    say("accumulate/determinism", label)
+    x = c["X"][:4].contiguous()
+    idx, count = ps.predict(c["P"], x, c["ws"])
+    y1 = ps.sparse_ffn(c["W"], x, idx, count, c["ws"])
+    idx2, count2 = ps.predict(c["P"], x, c["ws"])
+    y2 = ps.sparse_ffn(c["W"], x, idx2, count2, c["ws"])
+    torch.cuda.synchronize()
+    n = int(count.item())
+    assert int(count2.item()) == n and torch.equal(idx[:n], idx2[:n])
+    assert torch.equal(y1, y2)
+    base = torch.randn(4, c["spec"].d, generator=torch.Generator().manual_seed(2)).to(DEV)
+    acc = base.clone()
+    ps.sparse_ffn(c["W"], x, idx, count, c["ws"], y=acc, accumulate=True)
+    assert torch.equal(acc, base + y1)
+
+
+@pytest.mark.parametrize("B,F", [(1, 1), (1, 255), (3, 256), (5, 1000), (32, 4097)])
+def test_compact_given_logits(B, F):
+    say("compact", B, F)
+    g = torch.Generator().manual_seed(B * 1000 + F)
+    lg = torch.randn(B, F, generator=g, dtype=torch.float32) - 1.5
+    lg[:, ::7] = 0.0  # exactly at the threshold: inactive
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    ps.workspace_init(ws)
+    idx, count = ps.compact(lg.to(DEV), ws)
+    ref = oracle.compact(lg.numpy().astype(np.float64), 0.0)
+    n = int(count.item())
+    assert n == len(ref)
+    assert np.array_equal(idx[:n].cpu().numpy(), ref)
+    idx, count = ps.compact(lg.to(DEV), ws, thr=0.5)
+    ref = oracle.compact(lg.numpy().astype(np.float64), float(np.float32(0.5)))
+    assert int(count.item()) == len(ref) and np.array_equal(idx[: len(ref)].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+def test_profile_counts(label):
+    c = setup_case(label)
+    say("profile counts", label)
+    T = 24
+    Xp = synth.make_tokens(c["spec"], T, seed=4, stream="profile", device=DEV)
+    Xpn = Xp.cpu().numpy()
+    got = ps.profile_counts(c["W"], Xp).cpu().numpy()
+    lo = c["orc"].fire_counts(Xpn, 1e-4)  # fires even with a margin
+    hi = c["orc"].fire_counts(Xpn, -1e-4)  # fires or lies within the margin
+    assert np.all(lo <= got) and np.all(got <= hi)
+    exact = lo == hi
+    assert np.array_equal(got[exact], c["orc"].fire_counts(Xpn)[exact])
+    say("  neurons decided within the margin:", int((~exact).sum()))
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+def test_permute_hot_first(label):
+    c = setup_case(label)
+    say("permute", label)
+    counts = synth.profile_like_counts(c["L"].p, 512, seed=3)
+    perm_ref = oracle.hot_first_perm(counts)
+    perm, W2, P2 = ps.permute_hot_first(torch.from_numpy(counts).to(DEV), c["W"], c["P"])
+    torch.cuda.synchronize()
+    assert np.array_equal(perm.cpu().numpy(), perm_ref)
+    Lp = c["L"].permuted(torch.from_numpy(perm_ref.astype(np.int64)))
+    for name in ("w_up", "w_gate", "w_dT", "s_up", "s_gate", "s_dT", "b_up", "b_gate"):
+        a, b = getattr(W2, name), getattr(Lp, name)
+        assert (a is None) == (b is None), name
+        if a is not None:
+            assert torch.equal(a, b), name
+    assert torch.equal(P2.Q, Lp.Q) and torch.equal(P2.c, Lp.c) and P2.A is c["P"].A
+    # each logit depends only on its own row: permuted logits are bit-identical
+    x = c["X"][:3].contiguous()
+    F = c["spec"].F
+    l1 = torch.empty(3, F, device=DEV)
+    l2 = torch.empty(3, F, device=DEV)
+    ps.predict(c["P"], x, c["ws"], logits=l1)
+    ps.predict(P2, x, c["ws"], logits=l2)
+    assert torch.equal(l2, l1[:, perm.long()])
+
+
+@pytest.mark.parametrize("B,d", [(1, 8192), (4, 1000), (32, 264), (3, 5)])
+def test_layernorm_f16(B, d):
+    say("layernorm", B, d)
+    g = torch.Generator().manual_seed(B + d)
+    x = (torch.randn(B, d, generator=g) * 3 + torch.randn(B, 1, generator=g) * 2).to(torch.float32)
+    got = ps.layernorm_f16(x.to(DEV)).cpu().numpy().astype(np.float64)
+    ref = oracle.layernorm(x.numpy(), 1e-5)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= ulp)

@@ -1,0 +1,115 @@
+"""GPU parity at the full sizes of the five synthetic workloads, on sampled tokens the oracle can
+compute one by one: active sets (bit-exact outside the 1e-6 logit band), FFN outputs on the
+oracle's own lists, and end-to-end predict -> sparse FFN on every sampled token whose GPU set
+equals the oracle's set."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import check_set, check_y, ffn_of, oracle_layer, pred_of, tol_for
+
+pytestmark = pytest.mark.gpu
+
+ps = pytest.importorskip("activation_sparse_ffn_psffn_amd")
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_tokens(L, n, X, B, ntok_y=None, hot_first_perm=None):
+    """Predict + sparse FFN on the GPU for the batch X [B][d]; check against the oracle."""
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    F = L.spec.F
+    logits = torch.empty(B, F, device=DEV)
+    idx, count = ps.predict(P, X, ws, logits=logits)
+    y = ps.sparse_ffn(W, X, idx, count, ws)
+    torch.cuda.synchronize()
+    Xn = X.cpu().numpy()
+    orc = oracle_layer(n, L.spec.act)
+    ref_logits = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    st = check_set(idx, count, ref_logits)
+    lst = oracle.compact(ref_logits)
+    tb = B if ntok_y is None else ntok_y
+    tol = tol_for(L.spec.storage)
+    y_ref = orc.sparse_ffn(Xn[:tb], lst)
+    # the sparse FFN on the oracle's list
+    y_o = ps.sparse_ffn(W, X, torch.from_numpy(lst).to(DEV), torch.tensor([len(lst)], dtype=torch.int32,
+                                                                          device=DEV), ws)
+    e1 = check_y(y_o.cpu().numpy()[:tb], y_ref, tol)
+    e2 = None
+    if st["exact"]:
+        e2 = check_y(y.cpu().numpy()[:tb], y_ref, tol)
+    say("  B=%d count=%d ref=%d in-band diffs=%d err(list)=%.2e err(end-to-end)=%s" % (
+        B, st["count"], st["ref_count"], st["in_band_diff"], e1, "skipped" if e2 is None else "%.2e" % e2))
+    return st
+
+
+def test_tiny_relu_f32_all_tokens():
+    spec = synth.CONFIGS["tiny_relu_f32"]
+    L = synth.make_layer(spec, seed=0, device=DEV)
+    n = L.numpy()
+    X = synth.make_tokens(spec, spec.tokens, seed=0, device=DEV)
+    exact = 0
+    for t in range(spec.tokens):
+        exact += run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"]
+    assert exact >= spec.tokens - 2
+
+
+def test_opt30b_relu_f16_hot_first():
+    spec = synth.CONFIGS["opt30b_relu_f16"]
+    say("generate", spec.name)
+    L0 = synth.make_layer(spec, seed=0, device=DEV)
+    counts = synth.profile_like_counts(L0.p, spec.profile_tokens, seed=0)
+    perm_ref = oracle.hot_first_perm(counts)
+    perm, W2, P2 = ps.permute_hot_first(torch.from_numpy(counts).to(DEV), ffn_of(L0, ps), pred_of(L0, ps))
+    torch.cuda.synchronize()
+    assert np.array_equal(perm.cpu().numpy(), perm_ref)
+    L = L0.permuted(torch.from_numpy(perm_ref.astype(np.int64)))
+    assert torch.equal(W2.w_up, L.w_up) and torch.equal(W2.w_dT, L.w_dT) and torch.equal(P2.Q, L.Q)
+    del W2, P2
+    n = L.numpy()
+    X = synth.make_tokens(spec, 6, seed=0, device=DEV)
+    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(6))
+    assert exact >= 4
+    # the offline profile at full size, one token, bracketed by the oracle's counts at +-1e-4
+    Xp = synth.make_tokens(spec, 1, seed=0, stream="profile", device=DEV)
+    got = ps.profile_counts(ffn_of(L, ps), Xp).cpu().numpy()
+    orc = oracle_layer(n, "relu")
+    lo, hi = orc.fire_counts(Xp.cpu().numpy(), 1e-4), orc.fire_counts(Xp.cpu().numpy(), -1e-4)
+    assert np.all(lo <= got) and np.all(got <= hi)
+
+
+def test_llama2_13b_swiglu_f16():
+    spec = synth.CONFIGS["llama2_13b_swiglu_f16"]
+    say("generate", spec.name)
+    L = synth.make_layer(spec, seed=0, device=DEV)
+    n = L.numpy()
+    X = synth.make_tokens(spec, 3, seed=0, device=DEV)
+    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(3))
+    assert exact >= 2
+
+
+def test_opt175b_relu_i4_batch1_and_batch8():
+    spec = synth.CONFIGS["opt175b_relu_i4"]
+    say("generate", spec.name)
+    L = synth.make_layer(spec, seed=0, device=DEV)
+    n = L.numpy()
+    X = synth.make_tokens(spec, 10, seed=0, device=DEV)
+    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(2))
+    st = run_tokens(L, n, X[2:10].contiguous(), 8, ntok_y=2)
+    assert exact >= 1
+
+
+@pytest.mark.parametrize("layer,B", [(0, 1), (47, 4), (23, 32)])
+def test_falcon40b_stack_layers(layer, B):
+    spec = synth.CONFIGS["falcon40b_stack_f16"]
+    say("generate", spec.name, "layer", layer, "density %.4f" % synth.layer_density(spec, 0, layer))
+    L = synth.make_layer(spec, seed=0, layer=layer, device=DEV)
+    n = L.numpy()
+    X = synth.make_tokens(spec, B, seed=layer, device=DEV)
+    run_tokens(L, n, X, B, ntok_y=min(B, 2))

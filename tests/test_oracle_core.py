@@ -279,6 +279,8 @@ def test_fire_counts_match_numpy():
         else:
             z = n["w_gate"].astype(np.float64) @ X.astype(np.float64).T + n["b_gate"].astype(np.float64)[:, None]
         assert np.array_equal(cnt, (z > 0).sum(axis=1).astype(np.int32))
+        for t in (-0.3, 0.25):
+            assert np.array_equal(lay.fire_counts(X, t), (z > t).sum(axis=1).astype(np.int32))
 
 
 def test_hot_first_perm_is_stable_descending_bijection():
