@@ -8,8 +8,6 @@ using namespace psffn;
 
 namespace {
 
-constexpr size_t kStateBytes = 4096;  // reserved head of every workspace (kept zero between calls)
-
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 St st_of(psffn_dtype dt) { return dt == PSFFN_F32 ? St::F32 : (dt == PSFFN_F16 ? St::F16 : St::I4); }
@@ -23,6 +21,7 @@ bool batch_ok(int B) { return B >= 1 && B <= PSFFN_MAX_BATCH; }
 psffn_status check_pred(const psffn_predictor* P) {
   if (!P) return PSFFN_E_INVALID_ARG;
   if (P->d <= 0 || P->F <= 0 || P->r <= 0) return PSFFN_E_INVALID_ARG;
+  if (P->d > kMaxD || P->r > kMaxD) return PSFFN_E_UNSUPPORTED;
   if (P->dt != PSFFN_F32 && P->dt != PSFFN_F16) return PSFFN_E_UNSUPPORTED;
   if (P->d % 8 != 0 || P->r % 8 != 0) return PSFFN_E_UNSUPPORTED;
   if (!P->A || !P->Q || !P->c) return PSFFN_E_INVALID_ARG;
@@ -33,6 +32,7 @@ psffn_status check_pred(const psffn_predictor* P) {
 psffn_status check_ffn(const psffn_ffn* W) {
   if (!W) return PSFFN_E_INVALID_ARG;
   if (W->d <= 0 || W->F <= 0) return PSFFN_E_INVALID_ARG;
+  if (W->d > kMaxD) return PSFFN_E_UNSUPPORTED;
   if (W->dt != PSFFN_F32 && W->dt != PSFFN_F16 && W->dt != PSFFN_I4G128) return PSFFN_E_UNSUPPORTED;
   if (W->act != PSFFN_RELU && W->act != PSFFN_SWIGLU) return PSFFN_E_UNSUPPORTED;
   if (W->dt == PSFFN_I4G128 ? (W->d % 128 != 0) : (W->d % 8 != 0)) return PSFFN_E_UNSUPPORTED;
@@ -56,8 +56,8 @@ size_t ffn_scratch(int B, int d, int F) {
   return round256((size_t)F * B * 4) + round256((size_t)kSplitCap * B * (size_t)d * 4);
 }
 
-psffn_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
-  if (!ws || !aligned(ws, 256) || ws_bytes < kStateBytes + need) return PSFFN_E_WORKSPACE;
+psffn_status check_ws(const void* ws, size_t ws_bytes, int F, size_t need) {
+  if (!ws || !aligned(ws, 256) || ws_bytes < state_layout(F).scratch + need) return PSFFN_E_WORKSPACE;
   return PSFFN_OK;
 }
 
@@ -87,7 +87,9 @@ size_t psffn_workspace_bytes(const psffn_predictor* P, const psffn_ffn* W, int B
   if (!batch_ok(B) || (!P && !W)) return 0;
   if (P && check_pred(P) != PSFFN_OK) return 0;
   if (W && check_ffn(W) != PSFFN_OK) return 0;
-  size_t need = 0;
+  if (P && W && P->F != W->F) return 0;
+  const int F = P ? P->F : W->F;
+  size_t need = compact_scratch(F);
   if (P) {
     size_t v = predict_scratch(B, P->r, P->F);
     need = v > need ? v : need;
@@ -95,10 +97,8 @@ size_t psffn_workspace_bytes(const psffn_predictor* P, const psffn_ffn* W, int B
   if (W) {
     size_t v = ffn_scratch(B, W->d, W->F);
     need = v > need ? v : need;
-    v = compact_scratch(W->F);
-    need = v > need ? v : need;
   }
-  return kStateBytes + need;
+  return state_layout(F).scratch + need;
 }
 
 psffn_status psffn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -113,15 +113,19 @@ psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) ||
       (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
     return PSFFN_E_INVALID_ARG;
-  st = check_ws(ws, ws_bytes, predict_scratch(B, P->r, P->F));
+  st = check_ws(ws, ws_bytes, P->F, predict_scratch(B, P->r, P->F));
   if (st != PSFFN_OK) return st;
-  char* base = static_cast<char*>(ws) + kStateBytes;
-  float* h = reinterpret_cast<float*>(base);
-  uint8_t* flags = reinterpret_cast<uint8_t*>(base + round256((size_t)B * P->r * 4));
   const St pt = st_of(P->dt);
-  hipError_t e = launch_pred_h(pt, P->A, x, B, P->d, P->r, h, stream);
-  if (e == hipSuccess) e = launch_pred_logits(pt, P->Q, P->c, h, B, P->r, P->F, logit_thr, logits, flags, stream);
-  if (e == hipSuccess) e = launch_scatter(flags, P->F, idx, count, stream);
+  hipError_t e = hipErrorNotSupported;
+  if (B <= kFusedMaxBatch) e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream);
+  if (e == hipErrorNotSupported) {
+    char* base = static_cast<char*>(ws) + state_layout(P->F).scratch;
+    float* h = reinterpret_cast<float*>(base);
+    uint8_t* flags = reinterpret_cast<uint8_t*>(base + round256((size_t)B * P->r * 4));
+    e = launch_pred_h(pt, P->A, x, B, P->d, P->r, h, stream);
+    if (e == hipSuccess) e = launch_pred_logits(pt, P->Q, P->c, h, B, P->r, P->F, logit_thr, logits, flags, stream);
+    if (e == hipSuccess) e = launch_scatter(flags, P->F, idx, count, stream);
+  }
   return hip_status(e);
 }
 
@@ -130,9 +134,9 @@ psffn_status psffn_compact(const float* logits, int B, int F, float logit_thr, i
   if (!batch_ok(B) || F <= 0 || !logits || !aligned(logits, 4) || !idx || !aligned(idx, 4) || !count ||
       !aligned(count, 4) || logit_thr != logit_thr)
     return PSFFN_E_INVALID_ARG;
-  psffn_status st = check_ws(ws, ws_bytes, compact_scratch(F));
+  psffn_status st = check_ws(ws, ws_bytes, F, compact_scratch(F));
   if (st != PSFFN_OK) return st;
-  uint8_t* flags = static_cast<uint8_t*>(ws) + kStateBytes;
+  uint8_t* flags = static_cast<uint8_t*>(ws) + state_layout(F).scratch;
   hipError_t e = launch_flags_from_logits(logits, B, F, logit_thr, flags, stream);
   if (e == hipSuccess) e = launch_scatter(flags, F, idx, count, stream);
   return hip_status(e);
@@ -145,15 +149,19 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
       !aligned(y, 4))
     return PSFFN_E_INVALID_ARG;
-  st = check_ws(ws, ws_bytes, ffn_scratch(B, W->d, W->F));
+  st = check_ws(ws, ws_bytes, W->F, ffn_scratch(B, W->d, W->F));
   if (st != PSFFN_OK) return st;
-  char* base = static_cast<char*>(ws) + kStateBytes;
-  float* a = reinterpret_cast<float*>(base);
-  float* part = reinterpret_cast<float*>(base + round256((size_t)W->F * B * 4));
   const St wt = st_of(W->dt);
-  hipError_t e = launch_up(wt, W->act, *W, x, B, idx, count, a, stream);
-  if (e == hipSuccess) e = launch_down(wt, *W, a, B, idx, count, part, stream);
-  if (e == hipSuccess) e = launch_reduce(part, count, W->F, B, W->d, W->b_down, y, accumulate, stream);
+  hipError_t e = hipErrorNotSupported;
+  if (B <= kFusedMaxBatch) e = launch_ffn_fused(wt, *W, x, B, idx, count, y, accumulate, ws, stream);
+  if (e == hipErrorNotSupported) {
+    char* base = static_cast<char*>(ws) + state_layout(W->F).scratch;
+    float* a = reinterpret_cast<float*>(base);
+    float* part = reinterpret_cast<float*>(base + round256((size_t)W->F * B * 4));
+    e = launch_up(wt, W->act, *W, x, B, idx, count, a, stream);
+    if (e == hipSuccess) e = launch_down(wt, *W, a, B, idx, count, part, stream);
+    if (e == hipSuccess) e = launch_reduce(part, count, W->F, B, W->d, W->b_down, y, accumulate, stream);
+  }
   return hip_status(e);
 }
 

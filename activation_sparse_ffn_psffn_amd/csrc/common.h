@@ -5,7 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/psffn.h"
+#include "psffn.h"
 
 namespace psffn {
 
@@ -107,27 +107,36 @@ __device__ __forceinline__ float i4_elem(uint32_t w, int k) {
 
 // ----------------------------------------------------------------------------------------
 // workspace layout (bytes, every region 256-byte aligned)
+//
+//   [0, 256)      header words: call epoch, error bits
+//   chunk states  one 64-bit word per predictor chunk of >= 16 neurons, and one per group of 64
+//                 chunks (the two-level scan of the compaction), tagged with the call epoch so
+//                 that no reset is ever needed
+//   tile words    per-column-tile "partials done" counters of the down projection, left zero
+//                 by the last workgroup of each tile
+//   scratch       per-call buffers (h, flags, activations, partials); dead between calls
+// The layout depends on F only, so the predictor and the FFN of one layer can share one
+// workspace.  A fresh workspace must be zero-filled once (psffn_workspace_init).
 
-struct WsLayout {
-  size_t h = 0, flags = 0, act = 0, part = 0, total = 0;
-};
+constexpr int kMaxTiles = 1024;  // max column tiles of the down projection (d <= kMaxD)
+constexpr int kMaxD = 262144;
+constexpr int kMinChunk = 16;  // smallest predictor chunk (neurons)
+enum HeaderWord : int { kEpoch = 0, kErr = 3 };
 
 __host__ __device__ inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-inline WsLayout ws_layout(int d_pred, int r, int F, int d_ffn, int B) {
-  WsLayout L;
-  size_t off = 0;
-  L.h = off;
-  off += round256((size_t)B * (size_t)(r > 0 ? r : 0) * sizeof(float));
-  L.flags = off;
-  off += round256((size_t)(F > 0 ? F : 0) + 16);
-  L.act = off;
-  off += round256((size_t)(F > 0 ? F : 0) * (size_t)B * sizeof(float));
-  L.part = off;
-  off += round256((size_t)kSplitCap * (size_t)B * (size_t)(d_ffn > 0 ? d_ffn : 0) * sizeof(float));
-  L.total = off;
-  (void)d_pred;
-  return L;
+struct StateLayout {
+  size_t chunk_state, group_state, tile_done, scratch;
+};
+
+__host__ __device__ inline StateLayout state_layout(int F) {
+  StateLayout s;
+  const size_t chunks = (size_t)(F + kMinChunk - 1) / kMinChunk;
+  s.chunk_state = 256;
+  s.group_state = s.chunk_state + round256(8 * chunks);
+  s.tile_done = s.group_state + round256(8 * ((chunks + 63) / 64));
+  s.scratch = s.tile_done + round256(4 * (size_t)kMaxTiles);
+  return s;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -150,6 +159,16 @@ hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* perm, i
                               hipStream_t s);
 hipError_t launch_layernorm_f16(const float* x, int B, int d, float eps, void* out, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+// small-batch pipeline (batch <= kFusedMaxBatch): predictor in two kernels (h, then logits with
+// the ordered compaction), FFN in two kernels (up rows, then down tiles with the reduction).
+// They return hipErrorNotSupported when the shape is outside what they handle, and the caller
+// takes the generic kernels.
+constexpr int kFusedMaxBatch = 4;
+hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
+                                int32_t* count, float* logits, void* ws, hipStream_t s);
+hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
+                            float* y, int accumulate, void* ws, hipStream_t s);
 
 }  // namespace psffn
 
