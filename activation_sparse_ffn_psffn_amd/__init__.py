@@ -27,7 +27,7 @@ PSFFN_RELU, PSFFN_SWIGLU = 0, 1
 MAX_BATCH = 32
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libpsffn.so is not built (run: python -m activation_sparse_ffn_psffn_amd.build); "
+    raise ImportError("libpsffn.so is not built (run: python activation_sparse_ffn_psffn_amd/build.py); "
                       "there is no fallback implementation")
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -56,6 +56,8 @@ _lib.psffn_compact.restype = _i
 _lib.psffn_compact.argtypes = [_vp, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]
 _lib.psffn_sparse_ffn.restype = _i
 _lib.psffn_sparse_ffn.argtypes = [_P(_FFN), _vp, _i, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.psffn_layer.restype = _i
+_lib.psffn_layer.argtypes = [_P(_Predictor), _P(_FFN), _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.psffn_profile_counts.restype = _i
 _lib.psffn_profile_counts.argtypes = [_P(_FFN), _vp, _i, _vp, _vp]
 _lib.psffn_permute_hot_first.restype = _i
@@ -65,7 +67,8 @@ _lib.psffn_layernorm_f16.restype = _i
 _lib.psffn_layernorm_f16.argtypes = [_vp, _i, _i, _f, _vp, _vp]
 
 EXPORTED = ("psffn_status_str", "psffn_workspace_bytes", "psffn_workspace_init", "psffn_predict", "psffn_compact",
-            "psffn_sparse_ffn", "psffn_profile_counts", "psffn_permute_hot_first", "psffn_layernorm_f16")
+            "psffn_sparse_ffn", "psffn_layer", "psffn_profile_counts", "psffn_permute_hot_first",
+            "psffn_layernorm_f16")
 
 
 class PsffnError(RuntimeError):
@@ -200,6 +203,25 @@ def sparse_ffn(W: FFN, x: torch.Tensor, idx: torch.Tensor, count: torch.Tensor, 
     _check(_lib.psffn_sparse_ffn(ctypes.byref(s), _ptr(x), B, _ptr(idx), _ptr(count), _ptr(y), int(bool(accumulate)),
                                  _ptr(ws), ws.numel(), _stream(stream)), "sparse_ffn")
     return y
+
+
+def layer(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, idx: torch.Tensor = None,
+          count: torch.Tensor = None, logits: torch.Tensor = None, y: torch.Tensor = None, accumulate: bool = False,
+          stream=None):
+    """One decode step of one layer (predict + sparse FFN in one call): returns (idx, count, y)."""
+    B = x.shape[0]
+    F = P.Q.shape[0]
+    if idx is None:
+        idx = torch.empty(F, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if y is None:
+        y = torch.empty(B, W.d, dtype=torch.float32, device=x.device)
+    sp, sw = P.struct(), W.struct()
+    _check(_lib.psffn_layer(ctypes.byref(sp), ctypes.byref(sw), _ptr(x), B, float(thr), _ptr(idx), _ptr(count),
+                            _ptr(logits), _ptr(y), int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream)),
+           "layer")
+    return idx, count, y
 
 
 def profile_counts(W: FFN, X: torch.Tensor, counts: torch.Tensor = None, stream=None) -> torch.Tensor:

@@ -1,6 +1,6 @@
 """Build libpsffn.so in-tree with hipcc for gfx950.
 
-    python -m activation_sparse_ffn_psffn_amd.build
+    python activation_sparse_ffn_psffn_amd/build.py   (or __graft_entry__.build())
 
 Every HIP source is compiled with packed-fp32 instructions disabled (the compiler still emits
 plain and vector fp32 code), position independent, then linked into one shared library next to

@@ -165,6 +165,31 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
   return hip_status(e);
 }
 
+psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B, float logit_thr,
+                         int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  psffn_status st = check_pred(P);
+  if (st == PSFFN_OK) st = check_ffn(W);
+  if (st != PSFFN_OK) return st;
+  if (P->F != W->F || P->d != W->d) return PSFFN_E_INVALID_ARG;
+  if ((P->dt == PSFFN_F32) != (W->dt == PSFFN_F32)) return PSFFN_E_UNSUPPORTED;
+  if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
+      !aligned(y, 4) || (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
+    return PSFFN_E_INVALID_ARG;
+  size_t need = predict_scratch(B, P->r, P->F);
+  const size_t f = ffn_scratch(B, W->d, W->F);
+  need = f > need ? f : need;
+  st = check_ws(ws, ws_bytes, W->F, need);
+  if (st != PSFFN_OK) return st;
+  hipError_t e = hipErrorNotSupported;
+  if (B <= kFusedMaxBatch) e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
+  if (e != hipErrorNotSupported) return hip_status(e);
+  // shapes outside the one-call path: the two calls, same results
+  st = psffn_predict(P, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
+  if (st != PSFFN_OK) return st;
+  return psffn_sparse_ffn(W, x, B, idx, count, y, accumulate, ws, ws_bytes, stream);
+}
+
 psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int32_t* counts, hipStream_t stream) {
   psffn_status st = check_ffn(W);
   if (st != PSFFN_OK) return st;

@@ -112,6 +112,7 @@ __device__ __forceinline__ float i4_elem(uint32_t w, int k) {
 //   chunk states  one 64-bit word per predictor chunk of >= 16 neurons, and one per group of 64
 //                 chunks (the two-level scan of the compaction), tagged with the call epoch so
 //                 that no reset is ever needed
+//   mask words    one 32-bit word of active bits per 32 neurons (one-call layer path)
 //   tile words    per-column-tile "partials done" counters of the down projection, left zero
 //                 by the last workgroup of each tile
 //   scratch       per-call buffers (h, flags, activations, partials); dead between calls
@@ -126,7 +127,7 @@ enum HeaderWord : int { kEpoch = 0, kErr = 3 };
 __host__ __device__ inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct StateLayout {
-  size_t chunk_state, group_state, tile_done, scratch;
+  size_t chunk_state, group_state, masks, tile_done, scratch;
 };
 
 __host__ __device__ inline StateLayout state_layout(int F) {
@@ -134,7 +135,8 @@ __host__ __device__ inline StateLayout state_layout(int F) {
   const size_t chunks = (size_t)(F + kMinChunk - 1) / kMinChunk;
   s.chunk_state = 256;
   s.group_state = s.chunk_state + round256(8 * chunks);
-  s.tile_done = s.group_state + round256(8 * ((chunks + 63) / 64));
+  s.masks = s.group_state + round256(8 * ((chunks + 63) / 64));
+  s.tile_done = s.masks + round256(4 * (size_t)((F + 31) / 32));
   s.scratch = s.tile_done + round256(4 * (size_t)kMaxTiles);
   return s;
 }
@@ -169,6 +171,9 @@ hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, 
                                 int32_t* count, float* logits, void* ws, hipStream_t s);
 hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
                             float* y, int accumulate, void* ws, hipStream_t s);
+hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
+                              int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                              hipStream_t s);
 
 }  // namespace psffn
 

@@ -161,12 +161,13 @@ __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const 
 // loads are issued first; h (fp32, from the previous kernel) is read next; then logits, the
 // union test over the batch, and the chunk's place in the ascending list.
 
-template <St PT, int NB, int RV, int RPW>
+template <St PT, int NB, int RV, int RPW, bool MASKS>
 __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const float* __restrict__ c,
                                               const float* __restrict__ h, int r, int F, float thr, int nb,
                                               uint32_t* __restrict__ hdr, unsigned long long* __restrict__ cstate,
                                               unsigned long long* __restrict__ gstate, int32_t* __restrict__ idx,
-                                              int32_t* __restrict__ count, float* __restrict__ logits, int NQ) {
+                                              int32_t* __restrict__ count, float* __restrict__ logits, int NQ,
+                                              uint32_t* __restrict__ masks) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int ROWS = 4 * RPW;
@@ -234,6 +235,12 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
   }
   if (lane == 0) s_mask[wv] = mask;
   __syncthreads();
+  if constexpr (MASKS) {
+    // layer path: publish the chunk's active bits only; the up kernel orders them
+    static_assert(4 * RPW == 32, "one 32-bit mask word per chunk");
+    if (threadIdx.x == 0) masks[q] = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
+    return;
+  }
   int cnt = 0;
 #pragma unroll
   for (int w = 0; w < kBlock / kWave; ++w) cnt += __popc(s_mask[w]);
@@ -284,7 +291,14 @@ template <> struct DownTile<St::F32> { static constexpr int CPL = 4; };
 template <> struct DownTile<St::F16> { static constexpr int CPL = 8; };
 template <> struct DownTile<St::I4> { static constexpr int CPL = 16; };
 
+constexpr int kMaxScanChunks = 8192;  // chunks of 32 neurons the layer path can order (F <= 262144)
+
 struct FfnArgs {
+  const uint32_t* masks;  // layer path: per-chunk active bits from k_q
+  int32_t* idx_out;       // layer path: the ascending list written by k_up
+  int32_t* count_out;
+  int nq;
+  size_t xbytes;
   const void* w_up;
   const void* w_gate;
   const void* w_dT;
@@ -323,13 +337,73 @@ __device__ __forceinline__ int list_len(const int32_t* count, int F) {
 
 // k_up: a[k][b] for every listed neuron k < count (grid-stride, one wave per neuron).  The row
 // loads of the wave's first neuron go out before the workgroup stages x in LDS.
-template <St WT, psffn_act ACT, int NB>
+// SCAN mode of k_up: the chunk mask words are copied to LDS with coalesced loads (all in flight),
+// then s_pre[q] = number of active neurons in chunks before q, s_pre[nq] = total.
+__device__ void chunk_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t* s_mask, int* s_pre, int* s_red) {
+  for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * kBlock) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = q0 + u * kBlock < nq ? masks[q0 + u * kBlock] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u * kBlock < nq) s_mask[q0 + u * kBlock] = v[u];
+  }
+  __syncthreads();
+  const int per = (nq + kBlock - 1) / kBlock;  // consecutive chunks per thread
+  const int q0 = threadIdx.x * per;
+  int tot = 0;
+  for (int u = 0; u < per; ++u)
+    if (q0 + u < nq) tot += __popc(s_mask[q0 + u]);
+  // inclusive scan of the per-thread totals: within the wave, then across the 4 waves
+  const int lane = wave_lane(), wv = wave_id();
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) s_red[wv] = inc;
+  __syncthreads();
+  int run = inc - tot;
+  for (int w = 0; w < wv; ++w) run += s_red[w];
+  for (int u = 0; u < per; ++u)
+    if (q0 + u < nq) {
+      s_pre[q0 + u] = run;
+      run += __popc(s_mask[q0 + u]);
+    }
+  if (threadIdx.x == kBlock - 1) s_pre[nq] = run;
+  __syncthreads();
+}
+
+// neuron at list position k, from the chunk prefix and mask words in LDS (binary search + bit select)
+__device__ __forceinline__ int list_entry(const uint32_t* s_mask, const int* s_pre, int nq, int k) {
+  int lo = 0, hi = nq - 1;  // last chunk with s_pre[q] <= k
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
+  }
+  uint32_t m = s_mask[lo];
+  for (int j = k - s_pre[lo]; j > 0; --j) m &= m - 1u;  // drop the j lowest set bits
+  return lo * 32 + (int)__builtin_ctz(m);
+}
+
+template <St WT, psffn_act ACT, int NB, bool SCAN>
 __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int XSZ = WT == St::F32 ? 4 : 2;
   constexpr int UN = ACT == PSFFN_SWIGLU ? 8 : 16;
-  extern __shared__ uint4 s_x[];  // B * d activations (dynamic size)
-  const int n = list_len(g.count, g.F);
+  extern __shared__ uint4 s_x[];  // B * d activations, then (SCAN) the chunk prefix
+  __shared__ int s_red[kBlock / kWave];
+  int n;
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s_x) + g.xbytes);
+  int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
+  if constexpr (SCAN) {
+    chunk_prefix(g.masks, g.nq, s_mask, s_pre, s_red);
+    n = min(s_pre[g.nq], g.F);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n;
+  } else {
+    n = list_len(g.count, g.F);
+  }
   if (blockIdx.x * (kBlock / kWave) >= n) return;  // no neuron for this workgroup
   const int lane = wave_lane();
   const size_t rb = row_bytes<WT>(g.d);
@@ -337,7 +411,15 @@ __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
   bool staged = false;
   for (int k0 = blockIdx.x * (kBlock / kWave); k0 < n; k0 += gridDim.x * (kBlock / kWave)) {
     const int k = k0 + wave_id();
-    const int i = k < n ? g.idx[k] : -1;
+    int i = -1;
+    if constexpr (SCAN) {
+      if (k < n) {
+        i = list_entry(s_mask, s_pre, g.nq, k);
+        if (lane == 0) g.idx_out[k] = i;
+      }
+    } else {
+      i = k < n ? g.idx[k] : -1;
+    }
     const bool valid = (unsigned)i < (unsigned)g.F;
     const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)(valid ? i : 0) * rb;
     const char* grow =
@@ -563,8 +645,8 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
   if ((size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX) return hipErrorNotSupported;
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h, hdr);
-  k_q<PT, NB, RV, RPW><<<NQ, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, cstate, gstate, idx, count, logits,
-                                             NQ);
+  k_q<PT, NB, RV, RPW, false><<<NQ, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, cstate, gstate, idx, count,
+                                                    logits, NQ, nullptr);
   return hipGetLastError();
 }
 
@@ -596,19 +678,22 @@ hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, 
   return hipErrorNotSupported;
 }
 
-template <St WT, psffn_act ACT, int NB>
-static hipError_t ffn_t(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count, float* y,
-                        int accumulate, void* ws, hipStream_t s) {
-  // the largest split (all F neurons listed) must fit the LDS activation stage
+template <St WT>
+static bool ffn_fits(const psffn_ffn& W, int B) {
+  // the largest split (all F neurons listed) must fit the LDS activation stage, x must fit LDS
   int ks_max = (W.F + kSplitCap - 1) / kSplitCap;
   if (ks_max < 32) ks_max = 32;
-  if (ks_max * B > kActStage) return hipErrorNotSupported;
   constexpr int TW = kWave * DownTile<WT>::CPL;
-  const int T = (W.d + TW - 1) / TW;
-  if (T > kMaxTiles) return hipErrorNotSupported;
+  return ks_max * B <= kActStage && (W.d + TW - 1) / TW <= kMaxTiles &&
+         (size_t)B * W.d * (WT == St::F32 ? 4 : 2) <= (size_t)kStageX;
+}
+
+template <St WT>
+static FfnArgs ffn_args(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count, float* y,
+                        int accumulate, void* ws) {
   const StateLayout L = state_layout(W.F);
   char* w = static_cast<char*>(ws);
-  FfnArgs g;
+  FfnArgs g{};
   g.w_up = W.w_up;
   g.w_gate = W.w_gate;
   g.w_dT = W.w_dT;
@@ -630,12 +715,26 @@ static hipError_t ffn_t(const psffn_ffn& W, const void* x, int B, const int32_t*
   g.d = W.d;
   g.F = W.F;
   g.accumulate = accumulate;
-  if ((size_t)B * W.d * (WT == St::F32 ? 4 : 2) > (size_t)kStageX) return hipErrorNotSupported;
-  int up_grid = (W.F + 3) / 4;
+  g.xbytes = round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2));
+  return g;
+}
+
+template <St WT, psffn_act ACT, int NB, bool SCAN>
+static void ffn_launch(const FfnArgs& g, hipStream_t s) {
+  constexpr int TW = kWave * DownTile<WT>::CPL;
+  const int T = (g.d + TW - 1) / TW;
+  int up_grid = (g.F + 3) / 4;
   if (up_grid > 1024) up_grid = 1024;
-  const size_t xbytes = round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2));
-  k_up<WT, ACT, NB><<<up_grid, kBlock, xbytes, s>>>(g);
+  const size_t lds = g.xbytes + (SCAN ? 4 * (size_t)(2 * g.nq + 1) : 0);
+  k_up<WT, ACT, NB, SCAN><<<up_grid, kBlock, lds, s>>>(g);
   k_down<WT, NB><<<dim3(T, kSplitCap), kBlock, 0, s>>>(g);
+}
+
+template <St WT, psffn_act ACT, int NB>
+static hipError_t ffn_t(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count, float* y,
+                        int accumulate, void* ws, hipStream_t s) {
+  if (!ffn_fits<WT>(W, B)) return hipErrorNotSupported;
+  ffn_launch<WT, ACT, NB, false>(ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws), s);
   return hipGetLastError();
 }
 
@@ -658,6 +757,77 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
   if (st == St::F32) return ffn_nb<St::F32, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s);
   if (st == St::F16) return ffn_nb<St::F16, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s);
   return ffn_nb<St::I4, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s);
+}
+
+// ---- one decode step of one layer: k_h, k_q (mask words only), k_up (orders the list from the
+// masks, writes idx/count, computes the activations), k_down (partials + fixed-order reduce)
+
+template <St PT, St WT, psffn_act ACT, int NB, int RV>
+static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
+                          int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
+  constexpr int RPW = 8;
+  const int NQ = (P.F + 4 * RPW - 1) / (4 * RPW);
+  // k_up's LDS: the activations plus 8 bytes per chunk must fit the default 64 KB allocation
+  if (!ffn_fits<WT>(W, B) || NQ > kMaxScanChunks || (size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX ||
+      round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2)) + 8 * (size_t)NQ + 4 > (size_t)65536)
+    return hipErrorNotSupported;
+  const StateLayout L = state_layout(P.F);
+  char* w = static_cast<char*>(ws);
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
+  float* h = reinterpret_cast<float*>(w + L.scratch);
+  const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
+  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h, hdr);
+  k_q<PT, NB, RV, RPW, true><<<NQ, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, nullptr, nullptr, nullptr,
+                                                   nullptr, logits, NQ, masks);
+  FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
+  g.masks = masks;
+  g.nq = NQ;
+  g.idx_out = idx;
+  g.count_out = count;
+  ffn_launch<WT, ACT, NB, true>(g, s);
+  return hipGetLastError();
+}
+
+template <St PT, St WT, psffn_act ACT, int NB>
+static hipError_t layer_rv(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
+                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
+  const int per = kWave * Tr<PT>::EPL;
+  const int rv = (P.r + per - 1) / per;
+  if (rv == 1) return layer_t<PT, WT, ACT, NB, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (rv == 2) return layer_t<PT, WT, ACT, NB, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (rv == 3) return layer_t<PT, WT, ACT, NB, 3>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (rv == 4) return layer_t<PT, WT, ACT, NB, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  return hipErrorNotSupported;
+}
+
+template <St PT, St WT, psffn_act ACT>
+static hipError_t layer_nb(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
+                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
+  if (B == 1) return layer_rv<PT, WT, ACT, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (B == 2) return layer_rv<PT, WT, ACT, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (B <= 4) return layer_rv<PT, WT, ACT, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  return hipErrorNotSupported;
+}
+
+template <St PT, St WT>
+static hipError_t layer_act(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
+                            int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                            hipStream_t s) {
+  if (W.act == PSFFN_RELU) return layer_nb<PT, WT, PSFFN_RELU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  return layer_nb<PT, WT, PSFFN_SWIGLU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+}
+
+hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
+                              int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                              hipStream_t s) {
+  if (P.dt == PSFFN_F32 && W.dt == PSFFN_F32)
+    return layer_act<St::F32, St::F32>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (P.dt == PSFFN_F16 && W.dt == PSFFN_F16)
+    return layer_act<St::F16, St::F16>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (P.dt == PSFFN_F16 && W.dt == PSFFN_I4G128)
+    return layer_act<St::F16, St::I4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  return hipErrorNotSupported;
 }
 
 }  // namespace psffn

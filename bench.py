@@ -2,7 +2,9 @@
 """Benchmark of the predictor-gated sparse FFN decode step on one MI355X.
 
 A step is one decode token through one FFN layer: predict (h = A x, logits, threshold,
-compaction) then the sparse FFN over the predicted neurons.  The default workload is the
+compaction) then the sparse FFN over the predicted neurons, as one psffn_layer call.  The timed
+steps are replayed from HIP graphs (64 steps per graph); a second, eager pass brackets the two
+halves (psffn_predict, psffn_sparse_ffn) with HIP events for the per-call breakdown.  The default workload is the
 OPT-30B-shaped ReLU layer: d = 7168, F = 28672, predictor rank 1024, fp16 weights with fp32
 accumulation, batch 1, Zipf(1.1) firing at mean density 0.03, neurons permuted hot-first by a
 512-token profile.  Weights are random (synthetic); inputs are resident in HBM before timing.
@@ -56,7 +58,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=6)
-    ap.add_argument("--no-events", action="store_true", help="time only the whole region (no per-call events)")
+    ap.add_argument("--no-events", action="store_true", help="skip the per-call event pass")
+    ap.add_argument("--graph-steps", type=int, default=64,
+                    help="steps per captured HIP graph in the timed region (0: eager launches)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -107,30 +111,55 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def step(t, cnt, ev=None):
+    def step(t, cnt, stream):
+        # one decode step of one layer: predict + sparse FFN in one library call
+        Wc, Pc = copies[t % len(copies)]
+        ps.layer(Pc, Wc, X[t % ntok], ws, idx=idx, count=cnt, y=y, stream=stream)
+
+    def step_two_calls(t, cnt, ev):
         Wc, Pc = copies[t % len(copies)]
         x = X[t % ntok]
-        if ev is not None:
-            ev[0].record(stream)
+        ev[0].record(stream)
         ps.predict(Pc, x, ws, idx=idx, count=cnt, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        ev[1].record(stream)
         ps.sparse_ffn(Wc, x, idx, cnt, ws, y=y, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        ev[2].record(stream)
 
     scratch_cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     for t in range(Wm):
-        step(t, scratch_cnt)
+        step(t, scratch_cnt, stream)
     torch.cuda.synchronize()
 
-    evs = None if args.no_events else [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # the timed region: K steps replayed from HIP graphs of G consecutive steps (distinct tokens,
+    # rotating layer copies), so that host launch overhead is not part of the step
+    G = args.graph_steps
+    if G > 0:
+        if K % G:
+            raise SystemExit("--steps must be a multiple of --graph-steps")
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graphs = []
+        for g0 in range(0, K, G):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gr, stream=cap):
+                    for t in range(g0, g0 + G):
+                        step(Wm + t, counts_all[t:t + 1], cap)
+            graphs.append(gr)
+        stream.wait_stream(cap)
+        torch.cuda.synchronize()
+        graphs[0].replay()  # warm the replay path (outside the timed region)
+        torch.cuda.synchronize()
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e_start.record(stream)
-    for t in range(K):
-        step(Wm + t, counts_all[t:t + 1], None if evs is None else evs[t])
+    if G > 0:
+        for gr in graphs:
+            gr.replay()
+    else:
+        for t in range(K):
+            step(Wm + t, counts_all[t:t + 1], stream)
     e_end.record(stream)
     torch.cuda.synchronize()
     total_ms = e_start.elapsed_time(e_end)
@@ -142,16 +171,24 @@ def main():
     step_bytes = pred_bytes + ffn_bytes
     layer_gbps = step_bytes / (us_per_step * 1e-6) / 1e9
 
+    # per-call durations with HIP events on the launch stream: the same K steps, eager, as two calls
     roof = None
     breakdown = None
-    if evs is not None:
+    if not args.no_events:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        t0 = time.perf_counter()
+        for t in range(K):
+            step_two_calls(Wm + t, scratch_cnt, evs[t])
+        torch.cuda.synchronize()
         pred_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
         ffn_us = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
-        breakdown = {"predict_us": round(pred_us, 3), "sparse_ffn_us": round(ffn_us, 3)}
+        eager_us = (time.perf_counter() - t0) * 1e6 / K
+        breakdown = {"predict_us": round(pred_us, 3), "sparse_ffn_us": round(ffn_us, 3),
+                     "eager_two_call_step_us_wall": round(eager_us, 3)}
         achieved = pred_bytes / (pred_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "kernel": "psffn_predict (fp16 predictor stream: A then Q, threshold, compaction)",
+                "kernel": "psffn_predict (k_h + k_q: fp16 predictor stream A then Q, threshold, compaction)",
                 "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
 
     cpu = None

@@ -138,6 +138,14 @@ psffn_status psffn_compact(const float* logits, int B, int F, float logit_thr, i
 psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const int32_t* idx, const int32_t* count,
                               float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* One decode step of one layer: psffn_predict followed by psffn_sparse_ffn on its list, with
+ * the same outputs (idx ascending, count, optional logits, y) and the same requirements, in the
+ * fewest launches (the list is ordered inside the FFN's first kernel instead of by the predictor).
+ * P and W must describe the same layer (same F and d); P->dt is fp32 exactly when W->dt is fp32. */
+psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B, float logit_thr,
+                         int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* Offline activation profile (Summary, 2nd paragraph: models are profiled offline):
  * counts[i] = number of the T tokens X [T][d] for which neuron i truly fires -- the ReLU
  * pre-activation W_up[i].x + b_up[i] > 0, or for SwiGLU the gate W_gate[i].x + b_gate[i] > 0.

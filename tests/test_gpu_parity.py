@@ -222,3 +222,52 @@ def test_layernorm_f16(B, d):
     ref = oracle.layernorm(x.numpy(), 1e-5)
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
     assert np.all(np.abs(got - ref) <= ulp)
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_layer_call_equals_two_calls_and_oracle(label, B):
+    c = setup_case(label)
+    say("layer", label, "B", B)
+    x = c["X"][:B].contiguous()
+    F = c["spec"].F
+    idx1, cnt1 = ps.predict(c["P"], x, c["ws"])
+    y1 = ps.sparse_ffn(c["W"], x, idx1, cnt1, c["ws"])
+    logits = torch.empty(B, F, device=DEV)
+    idx2, cnt2, y2 = ps.layer(c["P"], c["W"], x, c["ws"], logits=logits)
+    torch.cuda.synchronize()
+    n = int(cnt1.item())
+    assert int(cnt2.item()) == n and torch.equal(idx1[:n], idx2[:n])
+    assert torch.equal(y1, y2)  # same kernels downstream of the list: bit-identical
+    ref = oracle.predict_logits(c["n"]["A"], c["n"]["Q"], c["n"]["c"], c["Xn"][:B])
+    st = check_set(idx2, cnt2, ref)
+    if st["exact"]:
+        check_y(y2.cpu().numpy(), c["orc"].sparse_ffn(c["Xn"][:B], oracle.compact(ref)), tol_for(c["spec"].storage))
+    # accumulate into a residual, twice in a row on one workspace
+    base = torch.randn(B, c["spec"].d, generator=torch.Generator().manual_seed(9)).to(DEV)
+    acc = base.clone()
+    ps.layer(c["P"], c["W"], x, c["ws"], y=acc, accumulate=True)
+    ps.layer(c["P"], c["W"], x, c["ws"], y=acc, accumulate=True)
+    assert torch.equal(acc, (base + y1) + y1)
+
+
+def test_layer_graph_replay_matches_eager():
+    c = setup_case("f16_relu")
+    x = c["X"][:1].contiguous()
+    idx, cnt, y = ps.layer(c["P"], c["W"], x, c["ws"])
+    y_ref = y.clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ps.layer(c["P"], c["W"], x, c["ws"], idx=idx, count=cnt, y=y)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), "replay %d differs" % rep
+        ps.layer(c["P"], c["W"], x, c["ws"])  # eager work between replays on the same workspace
+        torch.cuda.synchronize()
