@@ -3,8 +3,8 @@
 //   k_h     h = A x                       one wave per row of A, all of a row's loads in flight
 //   k_q     l = Q h + c, threshold, and the ascending active list by decoupled look-back
 //   k_up    a_k = act(W_up[idx[k]] . x (+ gate branch))   one wave per listed neuron
-//   k_down  column tile x k-split partial sums of a_k * W_dT[idx[k]], the last split of a tile
-//           adds the partials in split order and writes y
+//   k_down  column tile x k-split partial sums of a_k * W_dT[idx[k]]
+//   k_reduce_splits  y = b_down + the partials summed in split order (+ y when accumulating)
 //
 // Method ("PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU", Elamur
 // Research summary): Summary 2nd paragraph (a per-layer predictor guesses the firing neurons;
@@ -515,9 +515,9 @@ __device__ __forceinline__ void down_batch_load(const FfnArgs& g, int k0, int k_
 constexpr int kActStage = 4096;  // floats of LDS for one split's activations (rows x batch)
 
 // k_down: workgroup (tile, s) = column tile x k-split; its 4 waves take the split's rows round
-// robin (PF rows in flight per wave), are combined in wave order through LDS, and publish the
-// partial.  The last split of a tile to finish adds the S partials in split order, adds b_down,
-// writes y (or adds to it) and leaves the tile counter zero for the next call.
+// robin (PF rows in flight per wave) and are combined in wave order through LDS into the split's
+// partial.  (A last-arriving split reducing the tile inside this kernel was measured slower: the
+// coherent store, counter and load round trips cost ~8 us after the weights had streamed.)
 template <St WT, int NB>
 __global__ __launch_bounds__(kBlock) void k_down(FfnArgs g) {
   constexpr int CPL = DownTile<WT>::CPL;
@@ -525,7 +525,6 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs g) {
   constexpr int PF = 8;
   __shared__ float s_acc[NB * TW];
   __shared__ float s_a[kActStage];
-  __shared__ uint32_t s_last;
   const int n = list_len(g.count, g.F);
   int ks, S;
   ffn_split(n, ks, S);
@@ -585,7 +584,8 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs g) {
         }
     }
   }
-  // combine the 4 waves in wave order through LDS; wave 3 publishes the partial
+  // combine the 4 waves in wave order through LDS; the partial goes out with plain stores (the
+  // reduce kernel reads it after the kernel boundary)
   for (int step = 0; step < kBlock / kWave; ++step) {
     if (wv == step) {
 #pragma unroll
@@ -597,35 +597,32 @@ __global__ __launch_bounds__(kBlock) void k_down(FfnArgs g) {
           if (step < kBlock / kWave - 1)
             s_acc[at] = v;
           else if (live && b < g.B)
-            st_relaxed(&g.part[((size_t)s * g.B + b) * g.d + col0 + e], v);
+            g.part[((size_t)s * g.B + b) * g.d + col0 + e] = v;
         }
-      if (wv == kBlock / kWave - 1) stores_done();
     }
-    __syncthreads();
+    if (step < kBlock / kWave - 1) __syncthreads();
   }
-  if (threadIdx.x == 0) s_last = add_relaxed(&g.tile_done[tile], 1u) == (uint32_t)(S - 1);
-  __syncthreads();
-  if (!s_last) return;
-  // last partial of this tile: y = (y) + (b_down + sum_s part[s]) in split order
-  const int ncols = min(TW, g.d - tile * TW);
-  for (int q = threadIdx.x; q < NB * TW; q += kBlock) {
-    const int b = q / TW, cc = q % TW;
-    if (b >= g.B || cc >= ncols) continue;
-    const int col = tile * TW + cc;
-    float v = g.b_down ? g.b_down[col] : 0.f;
-    for (int s0 = 0; s0 < S; s0 += 32) {
-      float pv[32];
+}
+
+// k_reduce: y[b][j] = (accumulate ? y[b][j] : 0) + (b_down[j] + sum_{s < S} part[s][b][j]), the
+// sum in split order.  One thread per output; all of its partial loads in flight at once.
+__global__ __launch_bounds__(kBlock) void k_reduce_splits(FfnArgs g) {
+  const int n = list_len(g.count, g.F);
+  int ks, S;
+  ffn_split(n, ks, S);
+  const size_t t = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= (size_t)g.B * g.d) return;
+  const int b = (int)(t / g.d), col = (int)(t % g.d);
+  float v = g.b_down ? g.b_down[col] : 0.f;
+  for (int s0 = 0; s0 < S; s0 += 32) {
+    float pv[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        pv[u] = s0 + u < S ? ld_relaxed(&g.part[((size_t)(s0 + u) * g.B + b) * g.d + col]) : 0.f;
+    for (int u = 0; u < 32; ++u) pv[u] = s0 + u < S ? g.part[((size_t)(s0 + u) * g.B + b) * g.d + col] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (s0 + u < S) v += pv[u];
-    }
-    float* yp = g.y + (size_t)b * g.d + col;
-    *yp = g.accumulate ? *yp + v : v;
+    for (int u = 0; u < 32; ++u)
+      if (s0 + u < S) v += pv[u];
   }
-  if (threadIdx.x == 0) st_relaxed(&g.tile_done[tile], 0u);
+  g.y[t] = g.accumulate ? g.y[t] + v : v;
 }
 
 // =========================================================================================
@@ -728,6 +725,7 @@ static void ffn_launch(const FfnArgs& g, hipStream_t s) {
   const size_t lds = g.xbytes + (SCAN ? 4 * (size_t)(2 * g.nq + 1) : 0);
   k_up<WT, ACT, NB, SCAN><<<up_grid, kBlock, lds, s>>>(g);
   k_down<WT, NB><<<dim3(T, kSplitCap), kBlock, 0, s>>>(g);
+  k_reduce_splits<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g);
 }
 
 template <St WT, psffn_act ACT, int NB>
