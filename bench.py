@@ -79,6 +79,8 @@ def main():
     B = args.batch
     dev = "cuda"
     torch.cuda.init()
+    if spec.layers > 1:
+        return bench_stack(args, spec, ps, synth, np, torch)
     log("workload", spec.name, "B", B)
     t0 = time.time()
     L = synth.make_layer(spec, seed=0, device=dev)
@@ -209,6 +211,71 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def bench_stack(args, spec, ps, synth, np, torch):
+    """Decode through a stack of FFN layers: per layer x <- x + FFN(fp16(LayerNorm(x))), the FFN
+    restricted to the batch's predicted union set; one step moves B tokens through all layers.
+    Reported as tokens/s through the stack (higher is better)."""
+    B, dev, L = args.batch, "cuda", spec.layers
+    t0 = time.time()
+    layers = []
+    for l in range(L):
+        Ly = synth.make_layer(spec, seed=0, layer=l, device=dev)
+        layers.append((ps.Predictor(Ly.A, Ly.Q, Ly.c), ps.FFN(spec.act, Ly.w_up, Ly.w_dT, b_up=Ly.b_up),
+                       float(Ly.p.sum())))
+        del Ly
+    torch.cuda.synchronize()
+    log("stack of %d layers ready in %.1f s" % (L, time.time() - t0))
+    P0, W0, _ = layers[0]
+    ws = ps.new_workspace(P0, W0, B)
+    F, d = spec.F, spec.d
+    idx = torch.empty(F, dtype=torch.int32, device=dev)
+    cnts = torch.zeros(L, dtype=torch.int32, device=dev)
+    x = synth.make_residual(spec, B, seed=0, device=dev)
+    hbuf = torch.empty(B, d, dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(st):
+        for l, (P, W, _) in enumerate(layers):
+            ps.layernorm_f16(x, 1e-5, out=hbuf, stream=st)
+            ps.layer(P, W, hbuf, ws, idx=idx, count=cnts[l:l + 1], y=x, accumulate=True, stream=st)
+
+    for _ in range(max(1, args.warmup // 16)):
+        step(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step(cap)
+    stream.wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    K = max(1, args.steps // 16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    tok_s = B / (ms * 1e-3)
+    n = cnts.cpu().numpy().astype(np.float64)
+    byt = sum(sum(algorithmic_bytes(spec, B, n[l])) for l in range(L))
+    out = {"metric": "decode tokens/s through a stack of sparse FFN layers", "value": round(tok_s, 1),
+           "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": "%s: %d layers d=%d F=%d r=%d f16 relu, batch %d, per-layer density U(0.02,0.10) "
+                                  "Zipf(1.0), residual + LayerNorm between layers" % (spec.name, L, d, F, spec.r, B),
+                      "batch": B},
+           "layer": {"us_per_layer": round(ms * 1e3 / L, 3), "gbps": round(byt / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "mean_union_active_per_layer": round(float(n.mean()), 1),
+                     "algorithmic_bytes_per_step": int(byt)},
+           "roofline": None, "cpu_baseline": None}
     print(json.dumps(out), flush=True)
 
 
