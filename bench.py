@@ -28,6 +28,34 @@ METRIC = "sparse-FFN µs/layer and achieved HBM GB/s (% of roofline) at batch 1"
 HBM_PEAK_GBPS = 8000.0
 
 
+# HBM bytes per predictor call (k_h + k_q), from two rocprofv3 --pmc passes over this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the calls).  A plain device copy of
+# 512 MiB reads as 262156 KiB of FETCH_SIZE and 524288 KiB of WRITE_SIZE, so FETCH_SIZE is scaled
+# by 2.0 and WRITE_SIZE by 1.0.  A figure holds only for the kernel sources it was measured on
+# (hash below); after any change to them the traffic is reported as null until measured again.
+TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/fused.hip")
+TRAFFIC = {
+    # (workload, batch): fetch KiB k_h 7265.1 + k_q 28872.4, write KiB 8.0 + 32.9
+    ("opt30b_relu_f16", 1): {"sources": "2c1051b822e11a79", "bytes": 74051482},
+}
+
+
+def sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, B):
+    rec = TRAFFIC.get((workload, B))
+    if rec is None or rec["sources"] != sources_hash():
+        return None
+    return rec["bytes"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -59,6 +87,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=6)
     ap.add_argument("--no-events", action="store_true", help="skip the per-call event pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 8 times with a plain device copy and exit (reference "
+                         "kernel of known traffic for scaling hardware byte counters)")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="steps per captured HIP graph in the timed region (0: eager launches)")
     args = ap.parse_args()
@@ -74,6 +105,16 @@ def main():
 
     import activation_sparse_ffn_psffn_amd as ps
     import synth
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 8}), flush=True)
+        return
 
     spec = synth.CONFIGS[args.workload]
     B = args.batch
@@ -189,7 +230,8 @@ def main():
                      "eager_two_call_step_us_wall": round(eager_us, 3)}
         achieved = pred_bytes / (pred_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(spec.name, B),
                 "kernel": "psffn_predict (k_h + k_q: fp16 predictor stream A then Q, threshold, compaction)",
                 "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
 
