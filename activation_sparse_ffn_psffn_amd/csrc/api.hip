@@ -56,6 +56,24 @@ size_t ffn_scratch(int B, int d, int F) {
   return round256((size_t)F * B * 4) + round256((size_t)kSplitCap * B * (size_t)d * 4);
 }
 
+// scratch of a call, whichever pipeline its batch size takes
+size_t pred_need(const psffn_predictor& P, int B) {
+  size_t v = predict_scratch(B, P.r, P.F);
+  if (batch_supported_pred(P, B)) {
+    const size_t b = batch_scratch_bytes(B, P.d, P.r, P.F, PSFFN_F16, PSFFN_RELU, true, false);
+    v = b > v ? b : v;
+  }
+  return v;
+}
+size_t ffn_need(const psffn_ffn& W, int B) {
+  size_t v = ffn_scratch(B, W.d, W.F);
+  if (batch_supported_ffn(W, B)) {
+    const size_t b = batch_scratch_bytes(B, W.d, 0, W.F, W.dt, W.act, false, true);
+    v = b > v ? b : v;
+  }
+  return v;
+}
+
 psffn_status check_ws(const void* ws, size_t ws_bytes, int F, size_t need) {
   if (!ws || !aligned(ws, 256) || ws_bytes < state_layout(F).scratch + need) return PSFFN_E_WORKSPACE;
   return PSFFN_OK;
@@ -91,11 +109,11 @@ size_t psffn_workspace_bytes(const psffn_predictor* P, const psffn_ffn* W, int B
   const int F = P ? P->F : W->F;
   size_t need = compact_scratch(F);
   if (P) {
-    size_t v = predict_scratch(B, P->r, P->F);
+    size_t v = pred_need(*P, B);
     need = v > need ? v : need;
   }
   if (W) {
-    size_t v = ffn_scratch(B, W->d, W->F);
+    size_t v = ffn_need(*W, B);
     need = v > need ? v : need;
   }
   return state_layout(F).scratch + need;
@@ -113,11 +131,14 @@ psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) ||
       (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
     return PSFFN_E_INVALID_ARG;
-  st = check_ws(ws, ws_bytes, P->F, predict_scratch(B, P->r, P->F));
+  st = check_ws(ws, ws_bytes, P->F, pred_need(*P, B));
   if (st != PSFFN_OK) return st;
   const St pt = st_of(P->dt);
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch) e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream);
+  if (B <= kFusedMaxBatch)
+    e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream);
+  else
+    e = launch_predict_batch(*P, x, B, logit_thr, idx, count, logits, ws, stream);
   if (e == hipErrorNotSupported) {
     char* base = static_cast<char*>(ws) + state_layout(P->F).scratch;
     float* h = reinterpret_cast<float*>(base);
@@ -149,11 +170,14 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
       !aligned(y, 4))
     return PSFFN_E_INVALID_ARG;
-  st = check_ws(ws, ws_bytes, W->F, ffn_scratch(B, W->d, W->F));
+  st = check_ws(ws, ws_bytes, W->F, ffn_need(*W, B));
   if (st != PSFFN_OK) return st;
   const St wt = st_of(W->dt);
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch) e = launch_ffn_fused(wt, *W, x, B, idx, count, y, accumulate, ws, stream);
+  if (B <= kFusedMaxBatch)
+    e = launch_ffn_fused(wt, *W, x, B, idx, count, y, accumulate, ws, stream);
+  else
+    e = launch_ffn_batch(*W, x, B, idx, count, y, accumulate, ws, stream);
   if (e == hipErrorNotSupported) {
     char* base = static_cast<char*>(ws) + state_layout(W->F).scratch;
     float* a = reinterpret_cast<float*>(base);
@@ -176,13 +200,16 @@ psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const voi
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
       !aligned(y, 4) || (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
     return PSFFN_E_INVALID_ARG;
-  size_t need = predict_scratch(B, P->r, P->F);
-  const size_t f = ffn_scratch(B, W->d, W->F);
+  size_t need = pred_need(*P, B);
+  const size_t f = ffn_need(*W, B);
   need = f > need ? f : need;
   st = check_ws(ws, ws_bytes, W->F, need);
   if (st != PSFFN_OK) return st;
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch) e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
+  if (B <= kFusedMaxBatch)
+    e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
+  else
+    e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
   if (e != hipErrorNotSupported) return hip_status(e);
   // shapes outside the one-call path: the two calls, same results
   st = psffn_predict(P, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);

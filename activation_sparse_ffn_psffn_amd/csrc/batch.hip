@@ -1,0 +1,945 @@
+// Batch pipeline (4 < B <= 32; fp16 predictor, fp16 or 4-bit FFN weights) on MFMA tiles.
+//
+// With several tokens every weight element is used B times, which a wave can no longer feed
+// from its vector ALUs at HBM rate (B fp32 FMAs per 2-byte weight); matrix cores take the
+// products instead.  Every contraction is a v_mfma_f32_16x16x32_f16 over 16 weight rows (or
+// columns) x 16 tokens (the batch is padded to NBP = 16 or 32 token columns with zeros):
+//
+//   k_bh      partial h over 512-element chunks of d            h = A x          (16 rows / wave)
+//   k_bhred   h = sum of the chunks in chunk order, split into fp16 hi + lo parts
+//   k_bq      logits Q (h_hi + h_lo) + c, union test over the batch, one mask word per 32 neurons
+//   k_bscan   (predict call only) the ascending list from the mask words
+//   k_bup     up (and gate) rows of 64 listed neurons x one chunk of d; x staged in LDS
+//   k_bact    pre-activations summed over the chunks in chunk order, bias, ReLU / SiLU-gate
+//   k_bdown   column tiles x row splits of sum_k a_k W_dT[idx[k]], transposed through LDS
+//   k_breduce y = b_down + the split partials in split order (+ y when accumulating)
+//
+// Method ("PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU", Elamur
+// Research summary): Summary 2nd paragraph (per-layer predictor, neuron-level kernels that skip
+// the inactive neurons) and Interesting ideas I4 (whole rows and columns, no sparse format); a
+// batch shares the union of its tokens' predicted sets.
+//
+// Precision: weights and activations are fp16 (or exact small integers for 4-bit weights), so
+// every product is exact in the fp32 accumulator.  The fp32 values that feed a contraction (h for
+// the logits, the activations for the down projection) are split as v = hi + lo with hi, lo
+// fp16, which keeps 22 significant bits, and both halves are multiplied: the logits and outputs
+// stay at fp32 accuracy.
+//
+// MFMA operand layout (16x16x32, fp16; lane L, i = L % 16, g = L / 16): the A operand of lane L
+// holds A[i][8g .. 8g+8), the B operand B[8g .. 8g+8)[i], and the result D[4g + v][i], v < 4.
+// The k index of a contraction is free to permute as long as both operands agree; over d the
+// kernels use "block of 128, lane group g owns elements [32g, 32g+32), step s uses
+// [32g + 8s, 32g + 8s + 8)", so each lane reads 64 contiguous bytes of a row per block (16
+// bytes for 4-bit rows: one word of 8 nibbles per step).
+#include "common.h"
+
+namespace psffn {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4_t mma(h8_t a, h8_t b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ h8_t as_h8(uint4 v) { return __builtin_bit_cast(h8_t, v); }
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
+
+// A operand from one word of 8 nibbles e0..e7: [e0 e4 e1 e5 e2 e6 e3 e7] (exact small integers);
+// the activations are paired the same way by pair_x8.
+__device__ __forceinline__ h8_t i4_frag(uint32_t w) {
+  const half2_t p0 = i4_pair(w, 0), p1 = i4_pair(w, 4), p2 = i4_pair(w, 8), p3 = i4_pair(w, 12);
+  h8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// v = hi + lo, hi = fp16(v), lo = fp16(v - hi)
+__device__ __forceinline__ void split_hl(float v, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
+constexpr int kHChunk = 512;       // elements of d per partial h
+constexpr int kBatchMaxF = 98304;  // the up kernel's LDS (x chunk + list scan) stays under 64 KB
+constexpr int kBSplitCap = 16;      // max row splits of the down projection
+constexpr int kDPitch = 136;        // LDS bytes per row of a wave's 32 x 64 fp16 weight block
+
+// ---- arguments -------------------------------------------------------------------------------
+struct BArgs {
+  // predictor
+  const uint16_t* A;
+  const uint16_t* Q;
+  const float* c;
+  int r;
+  float thr;
+  float* logits;
+  float* hpart;
+  uint16_t* hhi;
+  uint16_t* hlo;
+  uint32_t* masks;
+  int nq;
+  int32_t* idx_out;
+  int32_t* count_out;
+  // shared
+  const uint16_t* x;
+  int B, d, F;
+  // FFN
+  const void* w_up;
+  const void* w_gate;
+  const void* w_dT;
+  const uint16_t* s_up;
+  const uint16_t* s_gate;
+  const uint16_t* s_dT;
+  const float* b_up;
+  const float* b_gate;
+  const float* b_down;
+  const int32_t* idx;
+  const int32_t* count;
+  float* upart;
+  float* gpart;
+  int ldk;  // row stride (neurons) of the per-token activation arrays: F rounded up to 32
+  float* aT;
+  uint16_t* ahi;
+  uint16_t* alo;
+  float* part;
+  float* y;
+  int accumulate;
+};
+
+__device__ __forceinline__ int blist_len(const int32_t* count, int F) {
+  const int n = *count;
+  return n < 0 ? 0 : (n > F ? F : n);
+}
+
+// Row splits of the down projection for a list of n neurons: the partials (S x B x d fp32) are
+// kept to about a quarter of the weight bytes the splits stream, and each split is a whole number
+// of 32-row steps.  S >= 1 (an empty list still writes one zero partial).
+__device__ __forceinline__ void bsplit(int n, int B, int d, int row_bytes, int& ks, int& S) {
+  long long want = (long long)n * row_bytes / ((long long)B * d * 16);
+  if (want < 1) want = 1;
+  if (want > kBSplitCap) want = kBSplitCap;
+  ks = (int)((n + want - 1) / want);
+  ks = (ks + 31) & ~31;
+  if (ks < 32) ks = 32;
+  S = n > 0 ? (n + ks - 1) / ks : 1;
+}
+
+// ---- list ordering from mask words (bit b of word q: neuron 32q + b is active) ----------------
+template <int NTH>
+__device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t* s_mask, int* s_pre, int* s_red) {
+  for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * NTH) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = q0 + u * NTH < nq ? masks[q0 + u * NTH] : 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u * NTH < nq) s_mask[q0 + u * NTH] = v[u];
+  }
+  __syncthreads();
+  const int per = (nq + NTH - 1) / NTH;  // consecutive words per thread
+  const int q0 = threadIdx.x * per;
+  int tot = 0;
+  for (int u = 0; u < per; ++u)
+    if (q0 + u < nq) tot += __popc(s_mask[q0 + u]);
+  const int lane = wave_lane(), wv = wave_id();
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
+  }
+  if (lane == kWave - 1) s_red[wv] = inc;
+  __syncthreads();
+  int run = inc - tot;
+  for (int w = 0; w < wv; ++w) run += s_red[w];
+  for (int u = 0; u < per; ++u)
+    if (q0 + u < nq) {
+      s_pre[q0 + u] = run;
+      run += __popc(s_mask[q0 + u]);
+    }
+  if (threadIdx.x == NTH - 1) s_pre[nq] = run;
+  __syncthreads();
+}
+
+// neuron at list position k (0 <= k < total): last word q with s_pre[q] <= k, then its bit
+__device__ __forceinline__ int mask_entry(const uint32_t* s_mask, const int* s_pre, int nq, int k) {
+  int lo = 0, hi = nq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
+  }
+  uint32_t m = s_mask[lo];
+  for (int j = k - s_pre[lo]; j > 0; --j) m &= m - 1u;
+  return lo * 32 + (int)__builtin_ctz(m);
+}
+
+// =============================================================================================
+// k_bh: wave (row tile rt, chunk kc): partial h over d-elements [512 kc, 512 kc + 512) of rows
+// [16 rt, 16 rt + 16).  Grid (ceil(r / 64), ceil(d / 512)), 4 row tiles per workgroup share
+// the chunk of x through L1.  hpart[kc][n][j], n < NBP (padded tokens contribute zeros).
+
+template <int NT>
+__global__ __launch_bounds__(kBlock) void k_bh(BArgs g) {
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
+  const int rt = blockIdx.x * 4 + wave_id();
+  const int kc = blockIdx.y;
+  if (rt * 16 >= g.r) return;
+  const int row = rt * 16 + li;
+  const int d = g.d;
+  const uint16_t* arow = g.A + (size_t)(row < g.r ? row : 0) * d;
+  uint4 w[4][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = kc * kHChunk + kb * 128 + lg * 32 + s * 8;
+      w[kb][s] = (row < g.r && e < d) ? ldg16(arow + e) : zero4();
+    }
+  f4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    uint4 xv[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int n = t * 16 + li, e = kc * kHChunk + kb * 128 + lg * 32 + s * 8;
+        xv[t][s] = (n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mma(as_h8(w[kb][s]), as_h8(xv[t][s]), acc[t]);
+  }
+  const int j0 = rt * 16 + 4 * lg;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float* dst = g.hpart + ((size_t)kc * (16 * NT) + t * 16 + li) * g.r + j0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (j0 + v < g.r) dst[v] = acc[t][v];
+  }
+}
+
+// k_bhred: h[n][j] = sum over chunks in chunk order; hi/lo fp16 parts [NBP][r] (zero for n >= B)
+__global__ __launch_bounds__(kBlock) void k_bhred(BArgs g, int ksh, int nbp) {
+  const int t = blockIdx.x * kBlock + threadIdx.x;
+  if (t >= nbp * g.r) return;
+  const int n = t / g.r;
+  float s = 0.f;
+  if (n < g.B) {
+    for (int k0 = 0; k0 < ksh; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = k0 + u < ksh ? g.hpart[(size_t)(k0 + u) * nbp * g.r + t] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < ksh) s += v[u];
+    }
+  }
+  _Float16 hi, lo;
+  split_hl(s, hi, lo);
+  g.hhi[t] = __builtin_bit_cast(uint16_t, hi);
+  g.hlo[t] = __builtin_bit_cast(uint16_t, lo);
+}
+
+// =============================================================================================
+// k_bq: wave u covers neurons [32u, 32u + 32) (two row tiles) over all of r, blocks of 128
+// software-pipelined (the next block's Q rows and h fragments are requested before the current
+// block's MFMAs).  Writes mask word u and, optionally, the logits.
+
+template <int NT>
+__global__ __launch_bounds__(kBlock) void k_bq(BArgs g) {
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
+  const int u = blockIdx.x * 4 + wave_id();
+  if (u * 32 >= g.F) return;
+  const int r = g.r;
+  const int nkb = (r + 127) / 128;
+  const uint16_t* qrow[2];
+  bool qok[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = u * 32 + t * 16 + li;
+    qok[t] = i < g.F;
+    qrow[t] = g.Q + (size_t)(qok[t] ? i : 0) * r;
+  }
+  uint4 qc[2][4], hc[NT][4], lc[NT][4];
+  uint4 qn[2][4], hn[NT][4], ln[NT][4];
+  auto load = [&](int kb, uint4 (&q)[2][4], uint4 (&hh)[NT][4], uint4 (&hl)[NT][4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = kb * 128 + lg * 32 + s * 8;
+      const bool in = e < r;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) q[t][s] = (in && qok[t]) ? ldg16(qrow[t] + e) : zero4();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const size_t o = (size_t)(t * 16 + li) * r + e;
+        hh[t][s] = in ? ldg16(g.hhi + o) : zero4();
+        hl[t][s] = in ? ldg16(g.hlo + o) : zero4();
+      }
+    }
+  };
+  f4_t acc[2][NT];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[a][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+  load(0, qc, hc, lc);
+  for (int kb = 0; kb < nkb; ++kb) {
+    if (kb + 1 < nkb) load(kb + 1, qn, hn, ln);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[a][t] = mma(as_h8(qc[a][s]), as_h8(hc[t][s]), acc[a][t]);
+          acc[a][t] = mma(as_h8(qc[a][s]), as_h8(lc[t][s]), acc[a][t]);
+        }
+    if (kb + 1 < nkb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) qc[a][s] = qn[a][s];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          hc[t][s] = hn[t][s];
+          lc[t][s] = ln[t][s];
+        }
+      }
+    }
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = u * 32 + a * 16 + 4 * lg + v;
+      const float ci = i < g.F ? g.c[i] : 0.f;
+      unsigned long long any = 0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int n = t * 16 + li;
+        const float l = acc[a][t][v] + ci;
+        const bool ok = n < g.B && i < g.F;
+        if (g.logits && ok) g.logits[(size_t)n * g.F + i] = l;
+        any |= __ballot(ok && l > g.thr);
+      }
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if ((any >> (16 * gg)) & 0xffffull) word |= 1u << (a * 16 + 4 * gg + v);
+    }
+  if (lane == 0) g.masks[u] = word;
+}
+
+// k_bscan: one workgroup orders the list: idx (ascending) and count from the mask words
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void k_bscan(BArgs g) {
+  extern __shared__ uint32_t s_dyn[];
+  uint32_t* s_mask = s_dyn;
+  int* s_pre = reinterpret_cast<int*>(s_dyn + g.nq);
+  __shared__ int s_red[kScanThreads / kWave];
+  mask_prefix<kScanThreads>(g.masks, g.nq, s_mask, s_pre, s_red);
+  const int total = min(s_pre[g.nq], g.F);
+  if (threadIdx.x == 0) *g.count_out = total;
+  for (int q = threadIdx.x; q < g.nq; q += kScanThreads) {
+    uint32_t m = s_mask[q];
+    int at = s_pre[q];
+    while (m) {
+      const int b = __builtin_ctz(m);
+      if (at < g.F) g.idx_out[at] = q * 32 + b;
+      ++at;
+      m &= m - 1u;
+    }
+  }
+}
+
+// =============================================================================================
+// k_bup: unit (row block rb, chunk kc): list positions [64 rb, 64 rb + 64) (16 per wave) x
+// d-elements [KC kc, KC kc + KC).  The chunk of x (all NBP token rows) is staged in LDS; the
+// partial pre-activations go to upart/gpart[kc][n][k].  Grid-stride over the units.  SCAN: the
+// list is ordered from the mask words first (each workgroup, from LDS) and written out.
+
+template <St WT> struct BUp;
+template <> struct BUp<St::F16> { static constexpr int LPB = 4; };  // 16-byte loads per lane per block
+template <> struct BUp<St::I4> { static constexpr int LPB = 1; };
+
+template <int NT, int KC>
+__host__ __device__ constexpr int bup_xpitch() { return KC * 2 + 16; }
+
+template <St WT, psffn_act ACT, int NT, int KC, bool SCAN>
+__global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
+  constexpr int NBP = 16 * NT;
+  constexpr int KB = KC / 128;
+  constexpr int LPB = BUp<WT>::LPB;
+  constexpr int XP = bup_xpitch<NT, KC>();
+  constexpr bool GATE = ACT == PSFFN_SWIGLU;
+  extern __shared__ uint4 s_dyn4[];
+  char* s_x = reinterpret_cast<char*>(s_dyn4);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_x + NBP * XP);
+  int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
+  __shared__ int s_red[kBlock / kWave];
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
+  const int d = g.d;
+  int n_list;
+  if constexpr (SCAN) {
+    mask_prefix<kBlock>(g.masks, g.nq, s_mask, s_pre, s_red);
+    n_list = min(s_pre[g.nq], g.F);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n_list;
+  } else {
+    n_list = blist_len(g.count, g.F);
+  }
+  const int nrb = (n_list + 63) / 64;
+  const int nkc = (d + KC - 1) / KC;
+  const int units = nrb * nkc;
+  const size_t rb_bytes = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
+  const int ng = d / 128;  // 4-bit scale groups per row
+  for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int rb = unit % nrb, kc = unit / nrb;
+    const int k = rb * 64 + wv * 16 + li;  // this lane's A row (list position)
+    int i = -1;
+    if (k < n_list) {
+      if constexpr (SCAN) {
+        i = mask_entry(s_mask, s_pre, g.nq, k);
+        if (kc == 0 && lg == 0) g.idx_out[k] = i;
+      } else {
+        i = g.idx[k];
+      }
+    }
+    const bool valid = (unsigned)i < (unsigned)g.F;
+    const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)(valid ? i : 0) * rb_bytes;
+    const char* grow = GATE ? reinterpret_cast<const char*>(g.w_gate) + (size_t)(valid ? i : 0) * rb_bytes : nullptr;
+    uint4 wu[KB][LPB], wg[KB][LPB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int s = 0; s < LPB; ++s) {
+        const int e = kc * KC + kb * 128 + lg * 32 + s * 8;
+        const bool in = valid && e < d;
+        const size_t off = WT == St::I4 ? (size_t)e / 2 : (size_t)e * 2;
+        wu[kb][s] = in ? ldg16(urow + off) : zero4();
+        if constexpr (GATE) wg[kb][s] = in ? ldg16(grow + off) : zero4();
+      }
+    // 4-bit: scales of the result rows 4 lg + v (their neurons come from lanes 4 lg + v)
+    float su[KB][4], sg[KB][4];
+    if constexpr (WT == St::I4) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int iv = __shfl(i, 4 * lg + v, kWave);
+        const bool ok = (unsigned)iv < (unsigned)g.F;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int G = (kc * KC) / 128 + kb;
+          su[kb][v] = (ok && G < ng) ? h2f(g.s_up[(size_t)iv * ng + G]) : 0.f;
+          if constexpr (GATE) sg[kb][v] = (ok && G < ng) ? h2f(g.s_gate[(size_t)iv * ng + G]) : 0.f;
+        }
+      }
+    }
+    // stage the chunk of x: rows n < NBP, elements [KC kc, KC kc + KC) (zero past B or d);
+    // 4-bit: each 8 elements paired as the weight nibbles are
+    __syncthreads();  // the previous unit's reads of s_x are done
+    {
+      constexpr int PIECES = NBP * KC / 8;
+      for (int p0 = threadIdx.x; p0 < PIECES; p0 += 8 * kBlock) {
+        uint4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int p = p0 + q * kBlock;
+          const int n = p / (KC / 8), e = kc * KC + (p % (KC / 8)) * 8;
+          v[q] = (p < PIECES && n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int p = p0 + q * kBlock;
+          if (p < PIECES) {
+            const int n = p / (KC / 8), el = (p % (KC / 8)) * 8;
+            *reinterpret_cast<uint4*>(s_x + n * XP + el * 2) = WT == St::I4 ? pair_x8(v[q]) : v[q];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    f4_t au[NT], ag[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) au[t] = ag[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f4_t tu[NT], tg[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tu[t] = tg[t] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int el = kb * 128 + lg * 32 + s * 8;
+        h8_t fu, fg;
+        if constexpr (WT == St::I4) {
+          const uint32_t wdu = s == 0 ? wu[kb][0].x : s == 1 ? wu[kb][0].y : s == 2 ? wu[kb][0].z : wu[kb][0].w;
+          fu = i4_frag(wdu);
+          if constexpr (GATE) {
+            const uint32_t wdg = s == 0 ? wg[kb][0].x : s == 1 ? wg[kb][0].y : s == 2 ? wg[kb][0].z : wg[kb][0].w;
+            fg = i4_frag(wdg);
+          }
+        } else {
+          fu = as_h8(wu[kb][s]);
+          if constexpr (GATE) fg = as_h8(wg[kb][s]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const h8_t xf = as_h8(*reinterpret_cast<const uint4*>(s_x + (t * 16 + li) * XP + el * 2));
+          if constexpr (WT == St::I4) {
+            tu[t] = mma(fu, xf, tu[t]);
+            if constexpr (GATE) tg[t] = mma(fg, xf, tg[t]);
+          } else {
+            au[t] = mma(fu, xf, au[t]);
+            if constexpr (GATE) ag[t] = mma(fg, xf, ag[t]);
+          }
+        }
+      }
+      if constexpr (WT == St::I4) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            au[t][v] = fmaf(su[kb][v], tu[t][v], au[t][v]);
+            if constexpr (GATE) ag[t][v] = fmaf(sg[kb][v], tg[t][v], ag[t][v]);
+          }
+      }
+    }
+    // partials: rows k0 .. k0+3 of token n, 16 bytes per lane
+    const int k0 = rb * 64 + wv * 16 + 4 * lg;
+    if (k0 < n_list) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const size_t o = ((size_t)kc * NBP + t * 16 + li) * g.ldk + k0;
+        *reinterpret_cast<float4*>(g.upart + o) = make_float4(au[t][0], au[t][1], au[t][2], au[t][3]);
+        if constexpr (GATE)
+          *reinterpret_cast<float4*>(g.gpart + o) = make_float4(ag[t][0], ag[t][1], ag[t][2], ag[t][3]);
+      }
+    }
+  }
+}
+
+// k_bact: a[n][k] for list positions k < roundup(count, 32) and tokens n < NBP (zero past the
+// list and for padded tokens): the chunk partials summed in chunk order, plus bias, activation.
+// Written as fp32 (4-bit down projection scales it per column group) and as fp16 hi/lo parts.
+template <psffn_act ACT>
+__global__ __launch_bounds__(kBlock) void k_bact(BArgs g, int nkc, int nbp) {
+  const int n_list = blist_len(g.count, g.F);
+  const int kpad = (n_list + 31) & ~31;
+  const int total = nbp * kpad;
+  for (int t = blockIdx.x * kBlock + threadIdx.x; t < total; t += gridDim.x * kBlock) {
+    const int n = t / kpad, k = t % kpad;
+    float a = 0.f;
+    if (k < n_list && n < g.B) {
+      const int i = g.idx[k];
+      if ((unsigned)i < (unsigned)g.F) {
+        float su = 0.f, sg = 0.f;
+        for (int c0 = 0; c0 < nkc; c0 += 8) {
+          float pu[8], pg[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const size_t o = ((size_t)(c0 + q) * nbp + n) * g.ldk + k;
+            pu[q] = c0 + q < nkc ? g.upart[o] : 0.f;
+            pg[q] = (ACT == PSFFN_SWIGLU && c0 + q < nkc) ? g.gpart[o] : 0.f;
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (c0 + q < nkc) {
+              su += pu[q];
+              if constexpr (ACT == PSFFN_SWIGLU) sg += pg[q];
+            }
+        }
+        su += g.b_up ? g.b_up[i] : 0.f;
+        if constexpr (ACT == PSFFN_SWIGLU) {
+          sg += g.b_gate ? g.b_gate[i] : 0.f;
+          a = sg / (1.f + expf(-sg)) * su;
+        } else {
+          a = su > 0.f ? su : 0.f;
+        }
+      }
+    }
+    const size_t o = (size_t)n * g.ldk + k;
+    g.aT[o] = a;
+    _Float16 hi, lo;
+    split_hl(a, hi, lo);
+    g.ahi[o] = __builtin_bit_cast(uint16_t, hi);
+    g.alo[o] = __builtin_bit_cast(uint16_t, lo);
+  }
+}
+
+// =============================================================================================
+// k_bdown: workgroup (column tile of 256, split s); wave w owns columns [col0, col0 + 64) and
+// walks the split's list positions in steps of 32 rows, 4 steps per batch of loads.  Each step's
+// 32 x 64 weight block goes through the wave's own LDS region (4-bit: decoded to fp16) and comes
+// back transposed as A operands (columns x rows); the B operands are the activations of the 32
+// rows (hi and lo parts; 4-bit: times the rows' scales of this column group).
+// partial[s][n][col] for n < B.
+
+template <St WT> struct BDown;
+template <> struct BDown<St::F16> { static constexpr int LPS = 4; };  // 16-byte loads per lane per step
+template <> struct BDown<St::I4> { static constexpr int LPS = 1; };
+
+template <St WT, int NT>
+__global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
+  constexpr int PF = 4;
+  constexpr int LPS = BDown<WT>::LPS;
+  __shared__ __align__(16) char s_w[kBlock / kWave][32 * kDPitch];
+  __shared__ __align__(16) float s_sc[kBlock / kWave][32];
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
+  const int d = g.d;
+  const int n_list = blist_len(g.count, g.F);
+  const int rowb = WT == St::I4 ? d / 2 + 2 * (d / 128) : 2 * d;
+  int ks, S;
+  bsplit(n_list, g.B, d, rowb, ks, S);
+  const int s = blockIdx.y;
+  if (s >= S) return;
+  const int col0 = blockIdx.x * 256 + wv * 64;
+  const int k_lo = s * ks, k_hi = min(n_list, k_lo + ks);
+  const int srow = lane >> 1, shalf = lane & 1;  // staging: row of the step, 32-column half
+  char* wbuf = s_w[wv];
+  f4_t acc[4][NT];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+  const size_t row_stride = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
+  const int ng = d / 128;
+  for (int kb0 = k_lo; kb0 < k_hi; kb0 += 32 * PF) {
+    int rows[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int k = kb0 + p * 32 + srow;
+      int i = k < k_hi ? g.idx[k] : -1;
+      rows[p] = (unsigned)i < (unsigned)g.F ? i : -1;
+    }
+    uint4 wr[PF][LPS];
+    float sc[PF];
+    uint4 bh[PF][NT][2], bl[PF][NT][2];  // activations: f16 hi/lo (one uint4 each) or fp32 (two)
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const char* wrow = reinterpret_cast<const char*>(g.w_dT) + (size_t)(rows[p] >= 0 ? rows[p] : 0) * row_stride;
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) {
+        const int c = col0 + shalf * 32 + q * 8;
+        const bool in = rows[p] >= 0 && c < d;
+        wr[p][q] = in ? ldg16(wrow + (WT == St::I4 ? (size_t)c / 2 : (size_t)c * 2)) : zero4();
+      }
+      sc[p] = 0.f;
+      if constexpr (WT == St::I4) {
+        const int G = col0 / 128;
+        if (rows[p] >= 0 && G < ng) sc[p] = h2f(g.s_dT[(size_t)rows[p] * ng + G]);
+      }
+      const int kk = kb0 + p * 32 + lg * 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const size_t o = (size_t)(t * 16 + li) * g.ldk + kk;
+        if (kb0 + p * 32 < k_hi) {
+          if constexpr (WT == St::I4) {
+            bh[p][t][0] = ldg16(g.aT + o);
+            bh[p][t][1] = ldg16(g.aT + o + 4);
+          } else {
+            bh[p][t][0] = ldg16(g.ahi + o);
+            bl[p][t][0] = ldg16(g.alo + o);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      if (kb0 + p * 32 >= k_hi) break;
+      // stage the 32 x 64 block: row srow, columns [32 shalf, 32 shalf + 32), as fp16
+      char* dst = wbuf + srow * kDPitch + shalf * 64;
+      if constexpr (WT == St::I4) {
+        const uint32_t wd[4] = {wr[p][0].x, wr[p][0].y, wr[p][0].z, wr[p][0].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // 8 nibbles -> 8 fp16 in column order
+          uint32_t o4[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const uint32_t lo = (wd[q] >> (8 * h)) & 0xFu, hi = (wd[q] >> (8 * h + 4)) & 0xFu;
+            const half2_t v = __builtin_bit_cast(half2_t, (lo | (hi << 16)) ^ 0x64086408u) -
+                              half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+            o4[h] = __builtin_bit_cast(uint32_t, v);
+          }
+          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(o4[0], o4[1]);
+          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(o4[2], o4[3]);
+        }
+        if (shalf == 0) s_sc[wv][srow] = sc[p];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(wr[p][q].x, wr[p][q].y);
+          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(wr[p][q].z, wr[p][q].w);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // B operands: rows 8 lg .. 8 lg + 8 of the step, token li (+16 t)
+      h8_t fb_hi[NT], fb_lo[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (WT == St::I4) {
+          const float4 a0 = __builtin_bit_cast(float4, bh[p][t][0]);
+          const float4 a1 = __builtin_bit_cast(float4, bh[p][t][1]);
+          const float4 s0 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8]);
+          const float4 s1 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8 + 4]);
+          const float pv[8] = {a0.x * s0.x, a0.y * s0.y, a0.z * s0.z, a0.w * s0.w,
+                               a1.x * s1.x, a1.y * s1.y, a1.z * s1.z, a1.w * s1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            _Float16 hi, lo;
+            split_hl(pv[j], hi, lo);
+            fb_hi[t][j] = hi;
+            fb_lo[t][j] = lo;
+          }
+        } else {
+          fb_hi[t] = as_h8(bh[p][t][0]);
+          fb_lo[t] = as_h8(bl[p][t][0]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        h8_t fa;
+        const char* src = wbuf + (lg * 8) * kDPitch + (m * 16 + li) * 2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fa[j] = *reinterpret_cast<const _Float16*>(src + j * kDPitch);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[m][t] = mma(fa, fb_hi[t], acc[m][t]);
+          acc[m][t] = mma(fa, fb_lo[t], acc[m][t]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // D[col 16 m + 4 lg + v][token li + 16 t]
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int c = col0 + m * 16 + 4 * lg;
+    if (c >= d) continue;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = t * 16 + li;
+      if (n < g.B)
+        *reinterpret_cast<float4*>(g.part + ((size_t)s * g.B + n) * d + c) =
+            make_float4(acc[m][t][0], acc[m][t][1], acc[m][t][2], acc[m][t][3]);
+    }
+  }
+}
+
+// k_breduce: y[n][j] = (accumulate ? y : 0) + (b_down[j] + sum over splits in split order)
+__global__ __launch_bounds__(kBlock) void k_breduce(BArgs g, int rowb) {
+  const int n_list = blist_len(g.count, g.F);
+  int ks, S;
+  bsplit(n_list, g.B, g.d, rowb, ks, S);
+  const size_t t = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= (size_t)g.B * g.d) return;
+  const int col = (int)(t % g.d);
+  float v = g.b_down ? g.b_down[col] : 0.f;
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    float pv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) pv[u] = s0 + u < S ? g.part[(size_t)(s0 + u) * g.B * g.d + t] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (s0 + u < S) v += pv[u];
+  }
+  g.y[t] = g.accumulate ? g.y[t] + v : v;
+}
+
+// =============================================================================================
+// host side
+
+// scratch layout of the batch pipeline (offsets from the workspace scratch start); the predictor
+// and the FFN regions overlap: a layer runs them in stream order
+struct BLayout {
+  size_t hpart, hhi, hlo, pred_end;
+  size_t upart, gpart, aT, ahi, alo, part, ffn_end;
+};
+
+static int nbp_of(int B) { return B <= 16 ? 16 : 32; }
+static int up_kc(St wt, int nbp) { return (wt == St::I4 && nbp == 16) ? 1024 : 512; }
+
+static BLayout blayout(int B, int d, int r, int F, St wt, bool gate) {
+  BLayout L{};
+  const int nbp = nbp_of(B);
+  const size_t ksh = (size_t)(d + kHChunk - 1) / kHChunk;
+  L.hpart = 0;
+  L.hhi = round256(ksh * nbp * r * 4);
+  L.hlo = L.hhi + round256((size_t)nbp * r * 2);
+  L.pred_end = L.hlo + round256((size_t)nbp * r * 2);
+  const size_t ldk = (size_t)((F + 31) & ~31);
+  const size_t nkc = (size_t)(d + up_kc(wt, nbp) - 1) / up_kc(wt, nbp);
+  L.upart = 0;
+  L.gpart = round256(nkc * nbp * ldk * 4);
+  L.aT = L.gpart + (gate ? L.gpart : 0);
+  L.ahi = L.aT + round256((size_t)nbp * ldk * 4);
+  L.alo = L.ahi + round256((size_t)nbp * ldk * 2);
+  L.part = L.alo + round256((size_t)nbp * ldk * 2);
+  L.ffn_end = L.part + round256((size_t)kBSplitCap * B * (size_t)d * 4);
+  return L;
+}
+
+size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_act act, bool pred, bool ffn) {
+  const St wt = wdt == PSFFN_I4G128 ? St::I4 : St::F16;
+  const BLayout L = blayout(B, d, r > 0 ? r : 8, F, wt, act == PSFFN_SWIGLU);
+  size_t need = 0;
+  if (pred) need = L.pred_end;
+  if (ffn && L.ffn_end > need) need = L.ffn_end;
+  return need;
+}
+
+bool batch_supported_pred(const psffn_predictor& P, int B) {
+  return B > kFusedMaxBatch && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF;
+}
+bool batch_supported_ffn(const psffn_ffn& W, int B) {
+  return B > kFusedMaxBatch && B <= 32 && (W.dt == PSFFN_F16 || W.dt == PSFFN_I4G128) && W.F <= kBatchMaxF;
+}
+
+static void pred_args(BArgs& g, const psffn_predictor& P, const void* x, int B, float thr, float* logits, void* ws) {
+  const StateLayout S = state_layout(P.F);
+  char* w = static_cast<char*>(ws);
+  const BLayout L = blayout(B, P.d, P.r, P.F, St::F16, false);
+  char* sc = w + S.scratch;
+  g.A = static_cast<const uint16_t*>(P.A);
+  g.Q = static_cast<const uint16_t*>(P.Q);
+  g.c = P.c;
+  g.r = P.r;
+  g.thr = thr;
+  g.logits = logits;
+  g.hpart = reinterpret_cast<float*>(sc + L.hpart);
+  g.hhi = reinterpret_cast<uint16_t*>(sc + L.hhi);
+  g.hlo = reinterpret_cast<uint16_t*>(sc + L.hlo);
+  g.masks = reinterpret_cast<uint32_t*>(w + S.masks);
+  g.nq = (P.F + 31) / 32;
+  g.x = static_cast<const uint16_t*>(x);
+  g.B = B;
+  g.d = P.d;
+  g.F = P.F;
+}
+
+static void ffn_args_b(BArgs& g, const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
+                       float* y, int accumulate, void* ws) {
+  const StateLayout S = state_layout(W.F);
+  char* w = static_cast<char*>(ws);
+  const St wt = W.dt == PSFFN_I4G128 ? St::I4 : St::F16;
+  const BLayout L = blayout(B, W.d, 8, W.F, wt, W.act == PSFFN_SWIGLU);
+  char* sc = w + S.scratch;
+  g.x = static_cast<const uint16_t*>(x);
+  g.B = B;
+  g.d = W.d;
+  g.F = W.F;
+  g.w_up = W.w_up;
+  g.w_gate = W.w_gate;
+  g.w_dT = W.w_dT;
+  g.s_up = static_cast<const uint16_t*>(W.s_up);
+  g.s_gate = static_cast<const uint16_t*>(W.s_gate);
+  g.s_dT = static_cast<const uint16_t*>(W.s_dT);
+  g.b_up = W.b_up;
+  g.b_gate = W.b_gate;
+  g.b_down = W.b_down;
+  g.idx = idx;
+  g.count = count;
+  g.ldk = (W.F + 31) & ~31;
+  g.upart = reinterpret_cast<float*>(sc + L.upart);
+  g.gpart = reinterpret_cast<float*>(sc + L.gpart);
+  g.aT = reinterpret_cast<float*>(sc + L.aT);
+  g.ahi = reinterpret_cast<uint16_t*>(sc + L.ahi);
+  g.alo = reinterpret_cast<uint16_t*>(sc + L.alo);
+  g.part = reinterpret_cast<float*>(sc + L.part);
+  g.y = y;
+  g.accumulate = accumulate;
+  g.masks = reinterpret_cast<uint32_t*>(w + S.masks);
+  g.nq = (W.F + 31) / 32;
+}
+
+template <int NT>
+static void pred_launch(const BArgs& g, hipStream_t s) {
+  const int nbp = 16 * NT;
+  const int ksh = (g.d + kHChunk - 1) / kHChunk;
+  k_bh<NT><<<dim3((g.r + 63) / 64, ksh), kBlock, 0, s>>>(g);
+  k_bhred<<<(nbp * g.r + kBlock - 1) / kBlock, kBlock, 0, s>>>(g, ksh, nbp);
+  k_bq<NT><<<(g.F + 127) / 128, kBlock, 0, s>>>(g);
+}
+
+template <St WT, psffn_act ACT, int NT, bool SCAN>
+static void ffn_launch_b(const BArgs& g, hipStream_t s) {
+  constexpr int NBP = 16 * NT;
+  constexpr int KC = (WT == St::I4 && NT == 1) ? 1024 : 512;
+  const int nkc = (g.d + KC - 1) / KC;
+  const size_t lds = (size_t)NBP * bup_xpitch<NT, KC>() + (SCAN ? 8 * (size_t)g.nq + 4 : 0);
+  int units = ((g.F + 63) / 64) * nkc;
+  if (units > 1024) units = 1024;
+  k_bup<WT, ACT, NT, KC, SCAN><<<units, kBlock, lds, s>>>(g);
+  int act_grid = (NBP * g.ldk + kBlock - 1) / kBlock;
+  if (act_grid > 1024) act_grid = 1024;
+  k_bact<ACT><<<act_grid, kBlock, 0, s>>>(g, nkc, NBP);
+  const int rowb = WT == St::I4 ? g.d / 2 + 2 * (g.d / 128) : 2 * g.d;
+  k_bdown<WT, NT><<<dim3((g.d + 255) / 256, kBSplitCap), kBlock, 0, s>>>(g);
+  k_breduce<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g, rowb);
+}
+
+template <St WT, psffn_act ACT, bool SCAN>
+static void ffn_launch_nt(const BArgs& g, hipStream_t s) {
+  if (g.B <= 16) ffn_launch_b<WT, ACT, 1, SCAN>(g, s);
+  else ffn_launch_b<WT, ACT, 2, SCAN>(g, s);
+}
+
+template <bool SCAN>
+static void ffn_dispatch(const psffn_ffn& W, const BArgs& g, hipStream_t s) {
+  if (W.dt == PSFFN_I4G128) {
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::I4, PSFFN_RELU, SCAN>(g, s);
+    else ffn_launch_nt<St::I4, PSFFN_SWIGLU, SCAN>(g, s);
+  } else {
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::F16, PSFFN_RELU, SCAN>(g, s);
+    else ffn_launch_nt<St::F16, PSFFN_SWIGLU, SCAN>(g, s);
+  }
+}
+
+hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
+                                int32_t* count, float* logits, void* ws, hipStream_t s) {
+  if (!batch_supported_pred(P, B)) return hipErrorNotSupported;
+  BArgs g{};
+  pred_args(g, P, x, B, thr, logits, ws);
+  g.idx_out = idx;
+  g.count_out = count;
+  if (B <= 16) pred_launch<1>(g, s);
+  else pred_launch<2>(g, s);
+  k_bscan<<<1, kScanThreads, 8 * (size_t)g.nq + 4, s>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
+                            float* y, int accumulate, void* ws, hipStream_t s) {
+  if (!batch_supported_ffn(W, B)) return hipErrorNotSupported;
+  BArgs g{};
+  ffn_args_b(g, W, x, B, idx, count, y, accumulate, ws);
+  ffn_dispatch<false>(W, g, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
+                              int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                              hipStream_t s) {
+  if (!batch_supported_pred(P, B) || !batch_supported_ffn(W, B)) return hipErrorNotSupported;
+  BArgs g{};
+  pred_args(g, P, x, B, thr, logits, ws);
+  if (B <= 16) pred_launch<1>(g, s);
+  else pred_launch<2>(g, s);
+  BArgs f{};
+  ffn_args_b(f, W, x, B, idx, count, y, accumulate, ws);
+  f.idx = idx;  // written by k_bup's scan before k_bact / k_bdown read it
+  f.idx_out = idx;
+  f.count_out = count;
+  f.count = count;
+  ffn_dispatch<true>(W, f, s);
+  return hipGetLastError();
+}
+
+}  // namespace psffn

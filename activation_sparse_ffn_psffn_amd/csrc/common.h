@@ -175,6 +175,19 @@ hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, cons
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
                               hipStream_t s);
 
+// batch pipeline (kFusedMaxBatch < B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA
+// tiles; the same NotSupported convention
+bool batch_supported_pred(const psffn_predictor& P, int B);
+bool batch_supported_ffn(const psffn_ffn& W, int B);
+size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_act act, bool pred, bool ffn);
+hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
+                                int32_t* count, float* logits, void* ws, hipStream_t s);
+hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
+                            float* y, int accumulate, void* ws, hipStream_t s);
+hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
+                              int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
+                              hipStream_t s);
+
 }  // namespace psffn
 
 namespace psffn {

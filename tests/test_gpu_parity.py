@@ -84,12 +84,13 @@ def test_sparse_ffn_on_oracle_list(label, B):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-def test_edge_lists(label):
+@pytest.mark.parametrize("B", [2, 8, 20])
+def test_edge_lists(label, B):
     c = setup_case(label)
-    say("edge lists", label)
+    say("edge lists", label, "B", B)
     F, d = c["spec"].F, c["spec"].d
-    x = c["X"][:2].contiguous()
-    xn = c["Xn"][:2]
+    x = c["X"][:B].contiguous()
+    xn = c["Xn"][:B]
     tol = tol_for(c["spec"].storage)
     # empty list: y = b_down exactly (and 0 without b_down)
     idx0 = torch.zeros(F, dtype=torch.int32, device=DEV)
@@ -99,7 +100,7 @@ def test_edge_lists(label):
     bd = torch.randn(d, generator=torch.Generator().manual_seed(5)).to(DEV)
     Wb = ps.FFN(**{**c["W"].__dict__, "b_down": bd})
     y = ps.sparse_ffn(Wb, x, idx0, cnt0, c["ws"])
-    assert torch.equal(y, bd.expand(2, d))
+    assert torch.equal(y, bd.expand(B, d))
     # all neurons = dense FFN
     alln = np.arange(F, dtype=np.int32)
     y = ps.sparse_ffn(c["W"], x, torch.from_numpy(alln).to(DEV), torch.tensor([F], dtype=torch.int32, device=DEV),
@@ -135,10 +136,11 @@ def test_perfect_predictor_list_gives_dense(label):
 
 
 @pytest.mark.parametrize("label", ["f16_relu", "i4_relu", "f16_swiglu"])
-def test_accumulate_and_determinism(label):
+@pytest.mark.parametrize("B", [4, 12])
+def test_accumulate_and_determinism(label, B):
     c = setup_case(label)
-    say("accumulate/determinism", label)
-    x = c["X"][:4].contiguous()
+    say("accumulate/determinism", label, "B", B)
+    x = c["X"][:B].contiguous()
     idx, count = ps.predict(c["P"], x, c["ws"])
     y1 = ps.sparse_ffn(c["W"], x, idx, count, c["ws"])
     idx2, count2 = ps.predict(c["P"], x, c["ws"])
@@ -147,7 +149,7 @@ def test_accumulate_and_determinism(label):
     n = int(count.item())
     assert int(count2.item()) == n and torch.equal(idx[:n], idx2[:n])
     assert torch.equal(y1, y2)
-    base = torch.randn(4, c["spec"].d, generator=torch.Generator().manual_seed(2)).to(DEV)
+    base = torch.randn(B, c["spec"].d, generator=torch.Generator().manual_seed(2)).to(DEV)
     acc = base.clone()
     ps.sparse_ffn(c["W"], x, idx, count, c["ws"], y=acc, accumulate=True)
     assert torch.equal(acc, base + y1)
@@ -225,7 +227,7 @@ def test_layernorm_f16(B, d):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [1, 3, 8])
+@pytest.mark.parametrize("B", [1, 3, 8, 20, 32])
 def test_layer_call_equals_two_calls_and_oracle(label, B):
     c = setup_case(label)
     say("layer", label, "B", B)
@@ -251,9 +253,11 @@ def test_layer_call_equals_two_calls_and_oracle(label, B):
     assert torch.equal(acc, (base + y1) + y1)
 
 
-def test_layer_graph_replay_matches_eager():
-    c = setup_case("f16_relu")
-    x = c["X"][:1].contiguous()
+@pytest.mark.parametrize("label,B", [("f16_relu", 1), ("f16_relu", 8), ("i4_swiglu", 24)])
+def test_layer_graph_replay_matches_eager(label, B):
+    c = setup_case(label)
+    say("graph replay", label, "B", B)
+    x = c["X"][:B].contiguous()
     idx, cnt, y = ps.layer(c["P"], c["W"], x, c["ws"])
     y_ref = y.clone()
     torch.cuda.synchronize()
