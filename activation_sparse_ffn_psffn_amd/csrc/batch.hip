@@ -7,8 +7,9 @@
 //
 //   k_bh      partial h over 512-element chunks of d            h = A x          (16 rows / wave)
 //   k_bhred   h = sum of the chunks in chunk order, split into fp16 hi + lo parts
-//   k_bq      logits Q (h_hi + h_lo) + c, union test over the batch, one mask word per 32 neurons
-//   k_bscan   (predict call only) the ascending list from the mask words
+//   k_bq_lds  logits Q (h_hi + h_lo) + c, union test over the batch, one mask word per 32 neurons
+//             (h in LDS; k_bq reads it from L2 when it does not fit)
+//   k_bscan   the ascending list and its length from the mask words (one workgroup)
 //   k_bup     up (and gate) rows of 64 listed neurons x one chunk of d; x staged in LDS
 //   k_bact    pre-activations summed over the chunks in chunk order, bias, ReLU / SiLU-gate
 //   k_bdown   column tiles x row splits of sum_k a_k W_dT[idx[k]], transposed through LDS
@@ -44,6 +45,31 @@ __device__ __forceinline__ f4_t mma(h8_t a, h8_t b, f4_t c) {
 __device__ __forceinline__ h8_t as_h8(uint4 v) { return __builtin_bit_cast(h8_t, v); }
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0, 0, 0, 0); }
+
+// Buffer loads (MUBUF): a resource holds the base and the byte size of an array, the lane gives a
+// 32-bit byte offset, and a read past the size returns zeros in hardware.  One VGPR of address per
+// lane instead of two, no predicate, and an out-of-range row reads as zeros.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // an offset past every buffer: the load returns zeros
+
+// Loads that are issued whatever the predicate: when it is false they read a block of zeros in
+// device memory instead.  No branch around the load and no select after it, so the compiler's
+// wait counting stays exact and a ring of loads in flight is not drained at every step.
+__device__ uint4 g_zero16[1] = {{0u, 0u, 0u, 0u}};  // never written
+
+__device__ __forceinline__ uint4 ld16_or0(const void* p, bool ok, const void*) {
+  return ldg16(ok ? p : static_cast<const void*>(g_zero16));
+}
+__device__ __forceinline__ uint32_t ld16b_or0(const uint16_t* p, bool ok, const uint16_t*) {
+  return (uint32_t)*(ok ? p : reinterpret_cast<const uint16_t*>(g_zero16));
+}
 
 // A operand from one word of 8 nibbles e0..e7: [e0 e4 e1 e5 e2 e6 e3 e7] (exact small integers);
 // the activations are paired the same way by pair_x8.
@@ -163,65 +189,54 @@ __device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t
   __syncthreads();
 }
 
-// neuron at list position k (0 <= k < total): last word q with s_pre[q] <= k, then its bit
-__device__ __forceinline__ int mask_entry(const uint32_t* s_mask, const int* s_pre, int nq, int k) {
-  int lo = 0, hi = nq - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
-  }
-  uint32_t m = s_mask[lo];
-  for (int j = k - s_pre[lo]; j > 0; --j) m &= m - 1u;
-  return lo * 32 + (int)__builtin_ctz(m);
-}
-
 // =============================================================================================
 // k_bh: wave (row tile rt, chunk kc): partial h over d-elements [512 kc, 512 kc + 512) of rows
-// [16 rt, 16 rt + 16).  Grid (ceil(r / 64), ceil(d / 512)), 4 row tiles per workgroup share
-// the chunk of x through L1.  hpart[kc][n][j], n < NBP (padded tokens contribute zeros).
+// [16 rt, 16 rt + 16).  Grid (ceil(d / 512), ceil(r / 64)): consecutive workgroups read consecutive
+// chunks of the same 64 rows; the 4 waves of a workgroup share the chunk of x through L1.  Every load of the wave (A rows, x fragments) is issued before the first
+// MFMA: one memory round trip per wave.  hpart[kc][n][j], n < NBP (padded tokens give zeros).
 
 template <int NT>
 __global__ __launch_bounds__(kBlock) void k_bh(BArgs g) {
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
-  const int rt = blockIdx.x * 4 + wave_id();
-  const int kc = blockIdx.y;
+  const int rt = blockIdx.y * 4 + wave_id();
+  const int kc = blockIdx.x;
   if (rt * 16 >= g.r) return;
   const int row = rt * 16 + li;
   const int d = g.d;
   const uint16_t* arow = g.A + (size_t)(row < g.r ? row : 0) * d;
-  uint4 w[4][4];
+  uint4 xv[NT][16], w[16];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int j = 0; j < 16; ++j) {
+    const int e = kc * kHChunk + (j >> 2) * 128 + lg * 32 + (j & 3) * 8;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = kc * kHChunk + kb * 128 + lg * 32 + s * 8;
-      w[kb][s] = (row < g.r && e < d) ? ldg16(arow + e) : zero4();
+    for (int t = 0; t < NT; ++t) {
+      const int n = t * 16 + li;
+      xv[t][j] = (n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
     }
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int e = kc * kHChunk + (j >> 2) * 128 + lg * 32 + (j & 3) * 8;
+    w[j] = (row < g.r && e < d) ? ldg16(arow + e) : zero4();
+  }
   f4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    uint4 xv[NT][4];
+  for (int j = 0; j < 16; ++j)
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int n = t * 16 + li, e = kc * kHChunk + kb * 128 + lg * 32 + s * 8;
-        xv[t][s] = (n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
-      }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mma(as_h8(w[kb][s]), as_h8(xv[t][s]), acc[t]);
-  }
+    for (int t = 0; t < NT; ++t) acc[t] = mma(as_h8(w[j]), as_h8(xv[t][j]), acc[t]);
   const int j0 = rt * 16 + 4 * lg;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float* dst = g.hpart + ((size_t)kc * (16 * NT) + t * 16 + li) * g.r + j0;
+    if (j0 + 3 < g.r) {
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+    } else {
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (j0 + v < g.r) dst[v] = acc[t][v];
+      for (int v = 0; v < 4; ++v)
+        if (j0 + v < g.r) dst[v] = acc[t][v];
+    }
   }
 }
 
@@ -337,6 +352,251 @@ __global__ __launch_bounds__(kBlock) void k_bq(BArgs g) {
   if (lane == 0) g.masks[u] = word;
 }
 
+// k_bq_lds: the same result as k_bq with h (hi and lo, all NBP token rows) staged once per
+// workgroup in LDS (up to 160 KB on gfx950); one workgroup of 8 waves per CU, each wave takes
+// units of 32 neurons and keeps kBqRing blocks of Q rows in flight (a ring of registers refilled
+// as each block is consumed), so a wave waits for HBM once per unit, not once per block.
+
+constexpr int kBqThreads = 512;
+constexpr int kBqRing = 4;
+
+__host__ __device__ inline int bq_pitch(int r) { return 2 * r + 16; }  // LDS bytes per token row
+
+template <int NT>
+__global__ __launch_bounds__(kBqThreads) void k_bq_lds(BArgs g) {
+  constexpr int NBP = 16 * NT;
+  constexpr int D = kBqRing;
+  extern __shared__ uint4 s_dyn4[];
+  char* s_hi = reinterpret_cast<char*>(s_dyn4);
+  const int r = g.r, hp = bq_pitch(r);
+  char* s_lo = s_hi + NBP * hp;
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
+  const int nwaves = gridDim.x * (kBqThreads / kWave);
+  const int nunits = (g.F + 31) / 32;
+  const int nkb = (r + 127) / 128;
+  int u = blockIdx.x * (kBqThreads / kWave) + wave_id();
+  uint4 q[D][2][4];
+  auto loadq = [&](int uu, int kb, uint4(&qq)[2][4]) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int i = uu * 32 + a * 16 + li;
+      const uint16_t* qr = g.Q + (size_t)(i < g.F ? i : 0) * r;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = kb * 128 + lg * 32 + s * 8;
+        qq[a][s] = ld16_or0(qr + e, i < g.F && e < r, g.Q);
+      }
+    }
+  };
+  // the first unit's Q blocks go out before h is staged (block indices clamped to the last one)
+  if (u < nunits) {
+#pragma unroll
+    for (int p = 0; p < D; ++p) loadq(u, p < nkb ? p : nkb - 1, q[p]);
+  }
+  {
+    const int per_row = r / 8;  // 16-byte pieces per token row
+    const int pieces = 2 * NBP * per_row;
+    for (int p0 = threadIdx.x; p0 < pieces; p0 += 8 * kBqThreads) {
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pc = p0 + k * kBqThreads;
+        const int part = pc / (NBP * per_row), rem = pc % (NBP * per_row);
+        const uint16_t* src = part == 0 ? g.hhi : g.hlo;
+        v[k] = ld16_or0(src + (size_t)rem * 8, pc < pieces, nullptr);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int pc = p0 + k * kBqThreads;
+        if (pc < pieces) {
+          const int part = pc / (NBP * per_row), rem = pc % (NBP * per_row);
+          const int n = rem / per_row, e8 = rem % per_row;
+          *reinterpret_cast<uint4*>((part == 0 ? s_hi : s_lo) + n * hp + e8 * 16) = v[k];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (; u < nunits; u += nwaves) {
+    f4_t acc[2][NT];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[a][t] = f4_t{0.f, 0.f, 0.f, 0.f};
+    // one 128-wide block of Q rows against h from LDS (Q row elements past r are zero)
+    auto block = [&](int kb, const uint4(&qq)[2][4]) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = kb * 128 + lg * 32 + s * 8;
+        const int ec = e < r ? e : 0;
+        uint4 hh[NT], hl[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int o = (t * 16 + li) * hp + ec * 2;
+          hh[t] = *reinterpret_cast<const uint4*>(s_hi + o);
+          hl[t] = *reinterpret_cast<const uint4*>(s_lo + o);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            acc[a][t] = mma(as_h8(qq[a][s]), as_h8(hh[t]), acc[a][t]);
+            acc[a][t] = mma(as_h8(qq[a][s]), as_h8(hl[t]), acc[a][t]);
+          }
+      }
+    };
+    // main groups: every block consumed refills its slot with the block D later (clamped)
+    int kb0 = 0;
+    for (; kb0 + D < nkb; kb0 += D) {
+#pragma unroll
+      for (int p = 0; p < D; ++p) {
+        block(kb0 + p, q[p]);
+        const int nx = kb0 + p + D;
+        loadq(u, nx < nkb ? nx : nkb - 1, q[p]);
+      }
+    }
+    // last group: no refills
+#pragma unroll
+    for (int p = 0; p < D; ++p)
+      if (kb0 + p < nkb) block(kb0 + p, q[p]);
+    uint32_t word = 0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int i = u * 32 + a * 16 + 4 * lg + v;
+        const float ci = i < g.F ? g.c[i] : 0.f;
+        unsigned long long any = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int n = t * 16 + li;
+          const float l = acc[a][t][v] + ci;
+          const bool ok = n < g.B && i < g.F;
+          if (g.logits && ok) g.logits[(size_t)n * g.F + i] = l;
+          any |= __ballot(ok && l > g.thr);
+        }
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+          if ((any >> (16 * gg)) & 0xffffull) word |= 1u << (a * 16 + 4 * gg + v);
+      }
+    if (lane == 0) g.masks[u] = word;
+    if (u + nwaves < nunits) {
+#pragma unroll
+      for (int p = 0; p < D; ++p) loadq(u + nwaves, p < nkb ? p : nkb - 1, q[p]);
+    }
+  }
+}
+
+// k_bq_full: as k_bq_lds, but a wave takes one row tile (16 neurons) at a time and requests all
+// of its Q rows at once (NKB blocks of 128, 16 full rows in flight: the DRAM pages of a tile are
+// read together), then runs the MFMAs against h in LDS.  h is stored zero-padded to NKB x 128
+// elements per token, so the Q bytes read past a row's end (the next row, or zeros past the
+// array) multiply zeros.  Writes the 16-bit half of the tile's mask word.
+
+__host__ __device__ inline int bq_full_pitch(int nkb) { return nkb * 256 + 16; }
+
+constexpr int kBqFullThreads = 512;  // one workgroup per CU, two waves per SIMD
+
+template <int NT, int NKB>
+__global__ __launch_bounds__(kBqFullThreads) void k_bq_full(BArgs g) {
+  constexpr int NBP = 16 * NT;
+  constexpr int HP = NKB * 256 + 16;
+  constexpr int WPG = kBqFullThreads / kWave;
+  extern __shared__ uint4 s_dyn4[];
+  char* s_hi = reinterpret_cast<char*>(s_dyn4);
+  char* s_lo = s_hi + NBP * HP;
+  const int r = g.r;
+  const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
+  const int nwaves = gridDim.x * WPG;
+  const int ntiles = (g.F + 15) / 16;
+  const __amdgpu_buffer_rsrc_t qr = rsrc(g.Q, (uint32_t)((size_t)g.F * r * 2));
+  const __amdgpu_buffer_rsrc_t cr = rsrc(g.c, (uint32_t)((size_t)g.F * 4));
+  int tt = blockIdx.x * WPG + wave_id();
+  uint4 q[NKB][4];
+  float4 cv;
+  // a tile's Q rows and the c of its result rows 4 lg + v, all requested at once (rows past F
+  // read as zeros)
+  auto load_tile = [&](int t) {
+    const int i0 = t * 16 + 4 * lg;
+    cv = __builtin_bit_cast(float4, bld16(cr, i0 < g.F ? (uint32_t)i0 * 4 : kNoRow));
+    const int i = t * 16 + li;
+    const uint32_t base = i < g.F ? (uint32_t)(((size_t)i * r + lg * 32) * 2) : kNoRow;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) q[kb][s] = bld16(qr, base + kb * 256 + s * 16);
+  };
+  if (tt < ntiles) load_tile(tt);  // the first tile goes out before h is staged
+  {
+    constexpr int PER_ROW = NKB * 16;  // 16-byte pieces per padded token row
+    constexpr int PIECES = 2 * NBP * PER_ROW;
+    const __amdgpu_buffer_rsrc_t hr = rsrc(g.hhi, (uint32_t)(NBP * r * 2));
+    const __amdgpu_buffer_rsrc_t lr = rsrc(g.hlo, (uint32_t)(NBP * r * 2));
+    for (int p0 = threadIdx.x; p0 < PIECES; p0 += 4 * kBqFullThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pc = p0 + k * kBqFullThreads;
+        const int part = pc / (NBP * PER_ROW), rem = pc % (NBP * PER_ROW);
+        const int n = rem / PER_ROW, e = (rem % PER_ROW) * 8;
+        const uint32_t off = (pc < PIECES && e < r) ? (uint32_t)((n * r + e) * 2) : kNoRow;
+        v[k] = bld16(part == 0 ? hr : lr, off);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pc = p0 + k * kBqFullThreads;
+        if (pc < PIECES) {
+          const int part = pc / (NBP * PER_ROW), rem = pc % (NBP * PER_ROW);
+          const int n = rem / PER_ROW, e8 = rem % PER_ROW;
+          *reinterpret_cast<uint4*>((part == 0 ? s_hi : s_lo) + n * HP + e8 * 16) = v[k];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (; tt < ntiles; tt += nwaves) {
+    f4_t acc[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) acc[u] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int e = kb * 128 + lg * 32 + s * 8;
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+          const int o = (u * 16 + li) * HP + e * 2;
+          const uint4 hh = *reinterpret_cast<const uint4*>(s_hi + o);
+          const uint4 hl = *reinterpret_cast<const uint4*>(s_lo + o);
+          acc[u] = mma(as_h8(q[kb][s]), as_h8(hh), acc[u]);
+          acc[u] = mma(as_h8(q[kb][s]), as_h8(hl), acc[u]);
+        }
+        // keep the LDS reads of later steps from being hoisted (register pressure)
+        if (s == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    const float cvv[4] = {cv.x, cv.y, cv.z, cv.w};
+    uint32_t half = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = tt * 16 + 4 * lg + v;
+      unsigned long long any = 0;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int n = u * 16 + li;
+        const float l = acc[u][v] + cvv[v];
+        const bool ok = n < g.B && i < g.F;
+        if (g.logits && ok) g.logits[(size_t)n * g.F + i] = l;
+        any |= __ballot(ok && l > g.thr);
+      }
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if ((any >> (16 * gg)) & 0xffffull) half |= 1u << (4 * gg + v);
+    }
+    if (lane == 0) reinterpret_cast<uint16_t*>(g.masks)[tt] = (uint16_t)half;
+    if (tt + nwaves < ntiles) load_tile(tt + nwaves);
+  }
+}
+
 // k_bscan: one workgroup orders the list: idx (ascending) and count from the mask words
 constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void k_bscan(BArgs g) {
@@ -362,58 +622,54 @@ __global__ __launch_bounds__(kScanThreads) void k_bscan(BArgs g) {
 // =============================================================================================
 // k_bup: unit (row block rb, chunk kc): list positions [64 rb, 64 rb + 64) (16 per wave) x
 // d-elements [KC kc, KC kc + KC).  The chunk of x (all NBP token rows) is staged in LDS; the
-// partial pre-activations go to upart/gpart[kc][n][k].  Grid-stride over the units.  SCAN: the
-// list is ordered from the mask words first (each workgroup, from LDS) and written out.
+// partial pre-activations go to upart/gpart[kc][n][k].  Grid-stride over the units.  Per unit the
+// x chunk (L2) is requested first, then the weight rows (HBM), so that the LDS staging does not
+// wait behind the weights.
 
 template <St WT> struct BUp;
 template <> struct BUp<St::F16> { static constexpr int LPB = 4; };  // 16-byte loads per lane per block
 template <> struct BUp<St::I4> { static constexpr int LPB = 1; };
 
-template <int NT, int KC>
+template <int KC>
 __host__ __device__ constexpr int bup_xpitch() { return KC * 2 + 16; }
 
-template <St WT, psffn_act ACT, int NT, int KC, bool SCAN>
+template <St WT, psffn_act ACT, int NT, int KC>
 __global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
   constexpr int NBP = 16 * NT;
   constexpr int KB = KC / 128;
   constexpr int LPB = BUp<WT>::LPB;
-  constexpr int XP = bup_xpitch<NT, KC>();
+  constexpr int XP = bup_xpitch<KC>();
   constexpr bool GATE = ACT == PSFFN_SWIGLU;
+  constexpr int PIECES = NBP * KC / 8;             // 16-byte pieces of the x chunk
+  constexpr int PPT = (PIECES + kBlock - 1) / kBlock;  // per thread
+  static_assert(KB <= 8, "scales of one unit row fit one 16-byte load");
   extern __shared__ uint4 s_dyn4[];
   char* s_x = reinterpret_cast<char*>(s_dyn4);
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_x + NBP * XP);
-  int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
-  __shared__ int s_red[kBlock / kWave];
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
   const int d = g.d;
-  int n_list;
-  if constexpr (SCAN) {
-    mask_prefix<kBlock>(g.masks, g.nq, s_mask, s_pre, s_red);
-    n_list = min(s_pre[g.nq], g.F);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n_list;
-  } else {
-    n_list = blist_len(g.count, g.F);
-  }
+  const int n_list = blist_len(g.count, g.F);
   const int nrb = (n_list + 63) / 64;
   const int nkc = (d + KC - 1) / KC;
   const int units = nrb * nkc;
   const size_t rb_bytes = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
   const int ng = d / 128;  // 4-bit scale groups per row
   for (int unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int rb = unit % nrb, kc = unit / nrb;
-    const int k = rb * 64 + wv * 16 + li;  // this lane's A row (list position)
-    int i = -1;
-    if (k < n_list) {
-      if constexpr (SCAN) {
-        i = mask_entry(s_mask, s_pre, g.nq, k);
-        if (kc == 0 && lg == 0) g.idx_out[k] = i;
-      } else {
-        i = g.idx[k];
-      }
+    const int kc = unit % nkc, rb = unit / nkc;  // consecutive units: consecutive chunks of the same rows
+    // this lane's A row (list position) first, then the x chunk (rows n < NBP, elements
+    // [KC kc, KC kc + KC), zero past B or d), then the weight rows once the neuron id is back
+    const int k = rb * 64 + wv * 16 + li;
+    const int i_raw = g.idx[k < n_list ? k : n_list - 1];
+    uint4 xs[PPT];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      const int pc = threadIdx.x + q * kBlock;
+      const int n = pc / (KC / 8), e = kc * KC + (pc % (KC / 8)) * 8;
+      xs[q] = ld16_or0(g.x + (size_t)n * d + e, pc < PIECES && n < g.B && e < d, g.x);
     }
-    const bool valid = (unsigned)i < (unsigned)g.F;
-    const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)(valid ? i : 0) * rb_bytes;
-    const char* grow = GATE ? reinterpret_cast<const char*>(g.w_gate) + (size_t)(valid ? i : 0) * rb_bytes : nullptr;
+    const bool valid = k < n_list && (unsigned)i_raw < (unsigned)g.F;
+    const int i = valid ? i_raw : 0;
+    const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)i * rb_bytes;
+    const char* grow = GATE ? reinterpret_cast<const char*>(g.w_gate) + (size_t)i * rb_bytes : nullptr;
     uint4 wu[KB][LPB], wg[KB][LPB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -422,48 +678,49 @@ __global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
         const int e = kc * KC + kb * 128 + lg * 32 + s * 8;
         const bool in = valid && e < d;
         const size_t off = WT == St::I4 ? (size_t)e / 2 : (size_t)e * 2;
-        wu[kb][s] = in ? ldg16(urow + off) : zero4();
-        if constexpr (GATE) wg[kb][s] = in ? ldg16(grow + off) : zero4();
+        wu[kb][s] = ld16_or0(urow + off, in, g.w_up);
+        if constexpr (GATE) wg[kb][s] = ld16_or0(grow + off, in, g.w_gate);
       }
-    // 4-bit: scales of the result rows 4 lg + v (their neurons come from lanes 4 lg + v)
-    float su[KB][4], sg[KB][4];
+    // 4-bit: this row's scales of the chunk's KB groups, packed in pairs, later handed to the
+    // lanes holding the result rows; groups past the row's end stay zero (so do their weights)
+    uint32_t su_w[4] = {0, 0, 0, 0}, sg_w[4] = {0, 0, 0, 0};
     if constexpr (WT == St::I4) {
+      const int G0 = (kc * KC) / 128;
+      const uint16_t* sp = g.s_up + (size_t)i * ng;
+      const uint16_t* gp = GATE ? g.s_gate + (size_t)i * ng : nullptr;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int iv = __shfl(i, 4 * lg + v, kWave);
-        const bool ok = (unsigned)iv < (unsigned)g.F;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int G = (kc * KC) / 128 + kb;
-          su[kb][v] = (ok && G < ng) ? h2f(g.s_up[(size_t)iv * ng + G]) : 0.f;
-          if constexpr (GATE) sg[kb][v] = (ok && G < ng) ? h2f(g.s_gate[(size_t)iv * ng + G]) : 0.f;
-        }
+      for (int j = 0; j < KB; ++j) {
+        const int G = G0 + j;
+        su_w[j / 2] |= ld16b_or0(sp + G, valid && G < ng, g.s_up) << (16 * (j & 1));
+        if constexpr (GATE) sg_w[j / 2] |= ld16b_or0(gp + G, valid && G < ng, g.s_gate) << (16 * (j & 1));
       }
     }
-    // stage the chunk of x: rows n < NBP, elements [KC kc, KC kc + KC) (zero past B or d);
-    // 4-bit: each 8 elements paired as the weight nibbles are
     __syncthreads();  // the previous unit's reads of s_x are done
-    {
-      constexpr int PIECES = NBP * KC / 8;
-      for (int p0 = threadIdx.x; p0 < PIECES; p0 += 8 * kBlock) {
-        uint4 v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int p = p0 + q * kBlock;
-          const int n = p / (KC / 8), e = kc * KC + (p % (KC / 8)) * 8;
-          v[q] = (p < PIECES && n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int p = p0 + q * kBlock;
-          if (p < PIECES) {
-            const int n = p / (KC / 8), el = (p % (KC / 8)) * 8;
-            *reinterpret_cast<uint4*>(s_x + n * XP + el * 2) = WT == St::I4 ? pair_x8(v[q]) : v[q];
-          }
-        }
+    for (int q = 0; q < PPT; ++q) {
+      const int pc = threadIdx.x + q * kBlock;
+      if (pc < PIECES) {
+        const int n = pc / (KC / 8), el = (pc % (KC / 8)) * 8;
+        *reinterpret_cast<uint4*>(s_x + n * XP + el * 2) = WT == St::I4 ? pair_x8(xs[q]) : xs[q];
       }
     }
     __syncthreads();
+    float su[KB][4], sg[KB][4];
+    if constexpr (WT == St::I4) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int w2 = 0; w2 < KB / 2; ++w2) {
+          const uint32_t pu = (uint32_t)__shfl((int)su_w[w2], 4 * lg + v, kWave);
+          su[2 * w2][v] = h2f(pu & 0xffffu);
+          su[2 * w2 + 1][v] = h2f(pu >> 16);
+          if constexpr (GATE) {
+            const uint32_t pg = (uint32_t)__shfl((int)sg_w[w2], 4 * lg + v, kWave);
+            sg[2 * w2][v] = h2f(pg & 0xffffu);
+            sg[2 * w2 + 1][v] = h2f(pg >> 16);
+          }
+        }
+    }
     f4_t au[NT], ag[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) au[t] = ag[t] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -573,22 +830,25 @@ __global__ __launch_bounds__(kBlock) void k_bact(BArgs g, int nkc, int nbp) {
 
 // =============================================================================================
 // k_bdown: workgroup (column tile of 256, split s); wave w owns columns [col0, col0 + 64) and
-// walks the split's list positions in steps of 32 rows, 4 steps per batch of loads.  Each step's
-// 32 x 64 weight block goes through the wave's own LDS region (4-bit: decoded to fp16) and comes
-// back transposed as A operands (columns x rows); the B operands are the activations of the 32
-// rows (hi and lo parts; 4-bit: times the rows' scales of this column group).
-// partial[s][n][col] for n < B.
+// walks the split's list positions in steps of 32 rows.  The split's neuron ids are staged in LDS
+// first; then a ring of D steps of loads (weight block, activation fragments, 4-bit scale) stays in
+// flight per wave, refilled as each step is consumed.  Each step's 32 x 64 weight block goes
+// through the wave's own LDS region (4-bit: decoded to fp16) and comes back transposed as A
+// operands (columns x rows); the B operands are the activations of the 32 rows (hi and lo parts;
+// 4-bit: times the rows' scales of this column group).  partial[s][n][col] for n < B.
 
 template <St WT> struct BDown;
-template <> struct BDown<St::F16> { static constexpr int LPS = 4; };  // 16-byte loads per lane per step
-template <> struct BDown<St::I4> { static constexpr int LPS = 1; };
+template <> struct BDown<St::F16> { static constexpr int LPS = 4; static constexpr int D = 4; };
+template <> struct BDown<St::I4> { static constexpr int LPS = 1; static constexpr int D = 8; };  // (4 with 32 tokens)
 
 template <St WT, int NT>
-__global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
-  constexpr int PF = 4;
+__global__ __launch_bounds__(kBlock) void k_bdown(BArgs g, int ks_cap) {
   constexpr int LPS = BDown<WT>::LPS;
+  constexpr int D = (WT == St::I4 && NT == 2) ? 4 : BDown<WT>::D;
+  constexpr int AB = WT == St::I4 ? 2 : 1;  // activation loads per token tile: fp32 x 8, or fp16 hi (+ lo)
   __shared__ __align__(16) char s_w[kBlock / kWave][32 * kDPitch];
   __shared__ __align__(16) float s_sc[kBlock / kWave][32];
+  extern __shared__ int s_idx[];
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
   const int d = g.d;
   const int n_list = blist_len(g.count, g.F);
@@ -598,66 +858,68 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
   const int s = blockIdx.y;
   if (s >= S) return;
   const int col0 = blockIdx.x * 256 + wv * 64;
-  const int k_lo = s * ks, k_hi = min(n_list, k_lo + ks);
+  const int k_lo = s * ks;
+  const int nrows = min(min(n_list, k_lo + ks) - k_lo, ks_cap);
+  for (int j = threadIdx.x; j < nrows; j += kBlock) {
+    const int i = g.idx[k_lo + j];
+    s_idx[j] = (unsigned)i < (unsigned)g.F ? i : -1;
+  }
+  __syncthreads();
+  const int nsteps = (nrows + 31) / 32;
   const int srow = lane >> 1, shalf = lane & 1;  // staging: row of the step, 32-column half
   char* wbuf = s_w[wv];
+  const size_t row_stride = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
+  const int ng = d / 128;
+  uint4 wr[D][LPS], ah[D][NT][AB], al[D][NT];
+  float sc[D];
+  auto load_step = [&](int st, uint4(&w)[LPS], uint4(&a_hi)[NT][AB], uint4(&a_lo)[NT], float& scale) {
+    const int rr = st * 32 + srow;
+    const int ir = s_idx[rr < nrows ? rr : 0];
+    const bool ok = rr < nrows && ir >= 0;
+    const int i = ok ? ir : 0;
+    const char* wrow = reinterpret_cast<const char*>(g.w_dT) + (size_t)i * row_stride;
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      const int c = col0 + shalf * 32 + q * 8;
+      w[q] = ld16_or0(wrow + (WT == St::I4 ? (size_t)c / 2 : (size_t)c * 2), ok && c < d, g.w_dT);
+    }
+    scale = 0.f;
+    if constexpr (WT == St::I4) {
+      const int G = col0 / 128;
+      scale = h2f(ld16b_or0(g.s_dT + (size_t)i * ng + G, ok && G < ng, g.s_dT));
+    }
+    const int kk = k_lo + st * 32 + lg * 8;  // < roundup(count, 32): zero-filled past the list
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t o = (size_t)(t * 16 + li) * g.ldk + kk;
+      if constexpr (WT == St::I4) {
+        a_hi[t][0] = ldg16(g.aT + o);
+        a_hi[t][1] = ldg16(g.aT + o + 4);
+      } else {
+        a_hi[t][0] = ldg16(g.ahi + o);
+        a_lo[t] = ldg16(g.alo + o);
+      }
+    }
+  };
   f4_t acc[4][NT];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f4_t{0.f, 0.f, 0.f, 0.f};
-  const size_t row_stride = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
-  const int ng = d / 128;
-  for (int kb0 = k_lo; kb0 < k_hi; kb0 += 32 * PF) {
-    int rows[PF];
+  if (nsteps == 0) {
+    // empty split: the zero partial below
+  } else {
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int k = kb0 + p * 32 + srow;
-      int i = k < k_hi ? g.idx[k] : -1;
-      rows[p] = (unsigned)i < (unsigned)g.F ? i : -1;
-    }
-    uint4 wr[PF][LPS];
-    float sc[PF];
-    uint4 bh[PF][NT][2], bl[PF][NT][2];  // activations: f16 hi/lo (one uint4 each) or fp32 (two)
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const char* wrow = reinterpret_cast<const char*>(g.w_dT) + (size_t)(rows[p] >= 0 ? rows[p] : 0) * row_stride;
-#pragma unroll
-      for (int q = 0; q < LPS; ++q) {
-        const int c = col0 + shalf * 32 + q * 8;
-        const bool in = rows[p] >= 0 && c < d;
-        wr[p][q] = in ? ldg16(wrow + (WT == St::I4 ? (size_t)c / 2 : (size_t)c * 2)) : zero4();
-      }
-      sc[p] = 0.f;
-      if constexpr (WT == St::I4) {
-        const int G = col0 / 128;
-        if (rows[p] >= 0 && G < ng) sc[p] = h2f(g.s_dT[(size_t)rows[p] * ng + G]);
-      }
-      const int kk = kb0 + p * 32 + lg * 8;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const size_t o = (size_t)(t * 16 + li) * g.ldk + kk;
-        if (kb0 + p * 32 < k_hi) {
-          if constexpr (WT == St::I4) {
-            bh[p][t][0] = ldg16(g.aT + o);
-            bh[p][t][1] = ldg16(g.aT + o + 4);
-          } else {
-            bh[p][t][0] = ldg16(g.ahi + o);
-            bl[p][t][0] = ldg16(g.alo + o);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      if (kb0 + p * 32 >= k_hi) break;
+    for (int p = 0; p < D; ++p) load_step(p < nsteps ? p : nsteps - 1, wr[p], ah[p], al[p], sc[p]);
+  }
+  // one step: stage the block in LDS, read it back transposed, 2 MFMAs per tile pair
+  auto step = [&](uint4(&w)[LPS], uint4(&a_hi)[NT][AB], uint4(&a_lo)[NT], float scale_v) {
       // stage the 32 x 64 block: row srow, columns [32 shalf, 32 shalf + 32), as fp16
       char* dst = wbuf + srow * kDPitch + shalf * 64;
       if constexpr (WT == St::I4) {
-        const uint32_t wd[4] = {wr[p][0].x, wr[p][0].y, wr[p][0].z, wr[p][0].w};
+        const uint32_t wd[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // 8 nibbles -> 8 fp16 in column order
           uint32_t o4[4];
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
@@ -669,23 +931,22 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
           *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(o4[0], o4[1]);
           *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(o4[2], o4[3]);
         }
-        if (shalf == 0) s_sc[wv][srow] = sc[p];
+        if (shalf == 0) s_sc[wv][srow] = scale_v;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(wr[p][q].x, wr[p][q].y);
-          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(wr[p][q].z, wr[p][q].w);
+          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(w[q].x, w[q].y);
+          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(w[q].z, w[q].w);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      // B operands: rows 8 lg .. 8 lg + 8 of the step, token li (+16 t)
       h8_t fb_hi[NT], fb_lo[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if constexpr (WT == St::I4) {
-          const float4 a0 = __builtin_bit_cast(float4, bh[p][t][0]);
-          const float4 a1 = __builtin_bit_cast(float4, bh[p][t][1]);
+          const float4 a0 = __builtin_bit_cast(float4, a_hi[t][0]);
+          const float4 a1 = __builtin_bit_cast(float4, a_hi[t][1]);
           const float4 s0 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8]);
           const float4 s1 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8 + 4]);
           const float pv[8] = {a0.x * s0.x, a0.y * s0.y, a0.z * s0.z, a0.w * s0.w,
@@ -698,8 +959,8 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
             fb_lo[t][j] = lo;
           }
         } else {
-          fb_hi[t] = as_h8(bh[p][t][0]);
-          fb_lo[t] = as_h8(bl[p][t][0]);
+          fb_hi[t] = as_h8(a_hi[t][0]);
+          fb_lo[t] = as_h8(a_lo[t]);
         }
       }
 #pragma unroll
@@ -716,8 +977,20 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+  };
+  // main groups refill each consumed slot with the step D later (clamped); the last group does not
+  int st0 = 0;
+  for (; st0 + D < nsteps; st0 += D) {
+#pragma unroll
+    for (int p = 0; p < D; ++p) {
+      step(wr[p], ah[p], al[p], sc[p]);
+      const int nx = st0 + p + D;
+      load_step(nx < nsteps ? nx : nsteps - 1, wr[p], ah[p], al[p], sc[p]);
     }
   }
+#pragma unroll
+  for (int p = 0; p < D; ++p)
+    if (st0 + p < nsteps) step(wr[p], ah[p], al[p], sc[p]);
   // D[col 16 m + 4 lg + v][token li + 16 t]
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -859,47 +1132,125 @@ static void ffn_args_b(BArgs& g, const psffn_ffn& W, const void* x, int B, const
   g.nq = (W.F + 31) / 32;
 }
 
-template <int NT>
-static void pred_launch(const BArgs& g, hipStream_t s) {
-  const int nbp = 16 * NT;
-  const int ksh = (g.d + kHChunk - 1) / kHChunk;
-  k_bh<NT><<<dim3((g.r + 63) / 64, ksh), kBlock, 0, s>>>(g);
-  k_bhred<<<(nbp * g.r + kBlock - 1) / kBlock, kBlock, 0, s>>>(g, ksh, nbp);
-  k_bq<NT><<<(g.F + 127) / 128, kBlock, 0, s>>>(g);
+// largest row split the down projection can take for lists of up to F neurons (bsplit: a split
+// is at most 2 B d 16 / rowb rows while it is below the cap of 16 splits, else F / 16, plus rounding)
+static int bsplit_ks_cap(int F, int B, int d, int rowb) {
+  const long long t1 = 2LL * B * d * 16 / rowb + 2;
+  long long v = t1 > F / 16 + 2 ? t1 : F / 16 + 2;
+  v = ((v + 31) & ~31LL) + 32;
+  const long long f32 = (F + 31) & ~31;
+  return (int)(v < f32 ? v : f32);
 }
 
-template <St WT, psffn_act ACT, int NT, bool SCAN>
+// LDS of the persistent logits kernel, 0 when h does not fit (then the kernel with h fragments
+// read from L2 runs instead)
+static size_t bq_lds(int nbp, int r) {
+  const size_t b = 2 * (size_t)nbp * bq_pitch(r);
+  return b <= (size_t)160 * 1024 ? b : 0;
+}
+
+template <int NT>
+static hipError_t bq_lds_attr() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bq_lds<NT>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return e;
+}
+
+template <int NT, int NKB>
+static hipError_t bq_full_attr() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bq_full<NT, NKB>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  return e;
+}
+
+static int cu_count() {
+  static const int n = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return v > 0 ? v : 256;
+  }();
+  return n;
+}
+
+template <int NT>
+static hipError_t pred_launch(const BArgs& g, hipStream_t s) {
+  const int nbp = 16 * NT;
+  const int ksh = (g.d + kHChunk - 1) / kHChunk;
+  k_bh<NT><<<dim3(ksh, (g.r + 63) / 64), kBlock, 0, s>>>(g);
+  k_bhred<<<(nbp * g.r + kBlock - 1) / kBlock, kBlock, 0, s>>>(g, ksh, nbp);
+  const size_t lds = bq_lds(nbp, g.r);
+  const int nkb = (g.r + 127) / 128;
+  const int nkb_t = nkb <= 4 ? 4 : (nkb <= 8 ? 8 : 12);
+  const size_t lds_full = 2 * (size_t)nbp * bq_full_pitch(nkb_t);
+  if (nkb <= 12 && lds_full <= (size_t)160 * 1024 && (size_t)g.F * g.r * 2 < (size_t)0xFFFFFFF0u) {
+    const int tiles = (g.F + 15) / 16, per_wg = kBqFullThreads / kWave;
+    int grid = cu_count();
+    if (grid > (tiles + per_wg - 1) / per_wg) grid = (tiles + per_wg - 1) / per_wg;
+    hipError_t e;
+    if (nkb <= 4) {
+      e = bq_full_attr<NT, 4>();
+      if (e == hipSuccess) k_bq_full<NT, 4><<<grid, kBqFullThreads, lds_full, s>>>(g);
+    } else if (nkb <= 8) {
+      e = bq_full_attr<NT, 8>();
+      if (e == hipSuccess) k_bq_full<NT, 8><<<grid, kBqFullThreads, lds_full, s>>>(g);
+    } else {
+      e = bq_full_attr<NT, 12>();
+      if (e == hipSuccess) k_bq_full<NT, 12><<<grid, kBqFullThreads, lds_full, s>>>(g);
+    }
+    if (e != hipSuccess) return e;
+  } else if (lds) {
+    const hipError_t e = bq_lds_attr<NT>();
+    if (e != hipSuccess) return e;
+    const int units = (g.F + 31) / 32, per_wg = kBqThreads / kWave;
+    int grid = cu_count();
+    if (grid > (units + per_wg - 1) / per_wg) grid = (units + per_wg - 1) / per_wg;
+    k_bq_lds<NT><<<grid, kBqThreads, lds, s>>>(g);
+  } else {
+    k_bq<NT><<<(g.F + 127) / 128, kBlock, 0, s>>>(g);
+  }
+  return hipSuccess;
+}
+
+template <St WT, psffn_act ACT, int NT>
 static void ffn_launch_b(const BArgs& g, hipStream_t s) {
   constexpr int NBP = 16 * NT;
   constexpr int KC = (WT == St::I4 && NT == 1) ? 1024 : 512;
   const int nkc = (g.d + KC - 1) / KC;
-  const size_t lds = (size_t)NBP * bup_xpitch<NT, KC>() + (SCAN ? 8 * (size_t)g.nq + 4 : 0);
+  const size_t lds = (size_t)NBP * bup_xpitch<KC>();
   int units = ((g.F + 63) / 64) * nkc;
   if (units > 1024) units = 1024;
-  k_bup<WT, ACT, NT, KC, SCAN><<<units, kBlock, lds, s>>>(g);
+  k_bup<WT, ACT, NT, KC><<<units, kBlock, lds, s>>>(g);
   int act_grid = (NBP * g.ldk + kBlock - 1) / kBlock;
   if (act_grid > 1024) act_grid = 1024;
   k_bact<ACT><<<act_grid, kBlock, 0, s>>>(g, nkc, NBP);
   const int rowb = WT == St::I4 ? g.d / 2 + 2 * (g.d / 128) : 2 * g.d;
-  k_bdown<WT, NT><<<dim3((g.d + 255) / 256, kBSplitCap), kBlock, 0, s>>>(g);
+  const int ks_cap = bsplit_ks_cap(g.F, g.B, g.d, rowb);
+  k_bdown<WT, NT><<<dim3((g.d + 255) / 256, kBSplitCap), kBlock, (size_t)ks_cap * 4, s>>>(g, ks_cap);
   k_breduce<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g, rowb);
 }
 
-template <St WT, psffn_act ACT, bool SCAN>
+template <St WT, psffn_act ACT>
 static void ffn_launch_nt(const BArgs& g, hipStream_t s) {
-  if (g.B <= 16) ffn_launch_b<WT, ACT, 1, SCAN>(g, s);
-  else ffn_launch_b<WT, ACT, 2, SCAN>(g, s);
+  if (g.B <= 16) ffn_launch_b<WT, ACT, 1>(g, s);
+  else ffn_launch_b<WT, ACT, 2>(g, s);
 }
 
-template <bool SCAN>
 static void ffn_dispatch(const psffn_ffn& W, const BArgs& g, hipStream_t s) {
   if (W.dt == PSFFN_I4G128) {
-    if (W.act == PSFFN_RELU) ffn_launch_nt<St::I4, PSFFN_RELU, SCAN>(g, s);
-    else ffn_launch_nt<St::I4, PSFFN_SWIGLU, SCAN>(g, s);
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::I4, PSFFN_RELU>(g, s);
+    else ffn_launch_nt<St::I4, PSFFN_SWIGLU>(g, s);
   } else {
-    if (W.act == PSFFN_RELU) ffn_launch_nt<St::F16, PSFFN_RELU, SCAN>(g, s);
-    else ffn_launch_nt<St::F16, PSFFN_SWIGLU, SCAN>(g, s);
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::F16, PSFFN_RELU>(g, s);
+    else ffn_launch_nt<St::F16, PSFFN_SWIGLU>(g, s);
   }
+}
+
+static hipError_t predict_and_scan(const BArgs& g, hipStream_t s) {
+  const hipError_t e = g.B <= 16 ? pred_launch<1>(g, s) : pred_launch<2>(g, s);
+  if (e != hipSuccess) return e;
+  k_bscan<<<1, kScanThreads, 8 * (size_t)g.nq + 4, s>>>(g);
+  return hipSuccess;
 }
 
 hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
@@ -909,10 +1260,8 @@ hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, 
   pred_args(g, P, x, B, thr, logits, ws);
   g.idx_out = idx;
   g.count_out = count;
-  if (B <= 16) pred_launch<1>(g, s);
-  else pred_launch<2>(g, s);
-  k_bscan<<<1, kScanThreads, 8 * (size_t)g.nq + 4, s>>>(g);
-  return hipGetLastError();
+  const hipError_t e = predict_and_scan(g, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
@@ -920,7 +1269,7 @@ hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int3
   if (!batch_supported_ffn(W, B)) return hipErrorNotSupported;
   BArgs g{};
   ffn_args_b(g, W, x, B, idx, count, y, accumulate, ws);
-  ffn_dispatch<false>(W, g, s);
+  ffn_dispatch(W, g, s);
   return hipGetLastError();
 }
 
@@ -930,15 +1279,13 @@ hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, cons
   if (!batch_supported_pred(P, B) || !batch_supported_ffn(W, B)) return hipErrorNotSupported;
   BArgs g{};
   pred_args(g, P, x, B, thr, logits, ws);
-  if (B <= 16) pred_launch<1>(g, s);
-  else pred_launch<2>(g, s);
+  g.idx_out = idx;
+  g.count_out = count;
+  hipError_t e = predict_and_scan(g, s);
+  if (e != hipSuccess) return e;
   BArgs f{};
   ffn_args_b(f, W, x, B, idx, count, y, accumulate, ws);
-  f.idx = idx;  // written by k_bup's scan before k_bact / k_bdown read it
-  f.idx_out = idx;
-  f.count_out = count;
-  f.count = count;
-  ffn_dispatch<true>(W, f, s);
+  ffn_dispatch(W, f, s);
   return hipGetLastError();
 }
 

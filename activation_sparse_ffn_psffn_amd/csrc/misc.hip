@@ -102,6 +102,50 @@ __global__ __launch_bounds__(kBlock) void k_layernorm_f16(const float* __restric
   for (int k = threadIdx.x; k < d; k += kBlock) o[k] = (_Float16)((xr[k] - mean) * inv);
 }
 
+// Same result definition, the row held in registers: every load of the row is issued at once
+// (K float4 per thread), then two block reductions (mean, then the centred sum of squares) on the
+// registers and one fp16 store pass.
+template <int K>
+__global__ __launch_bounds__(kBlock) void k_layernorm_f16_reg(const float* __restrict__ x, int d, float eps,
+                                                              _Float16* __restrict__ out) {
+  __shared__ float s_red[kBlock / kWave];
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)blockIdx.x * d);
+  const int n4 = d / 4;
+  float4 v[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = threadIdx.x + k * kBlock;
+    v[k] = j < n4 ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float sm = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) sm += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  const float mean = block_sum(sm, s_red) / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (threadIdx.x + k * kBlock < n4) {
+      const float a = v[k].x - mean, b = v[k].y - mean, c = v[k].z - mean, e = v[k].w - mean;
+      q = fmaf(a, a, q);
+      q = fmaf(b, b, q);
+      q = fmaf(c, c, q);
+      q = fmaf(e, e, q);
+    }
+  }
+  const float var = block_sum(q, s_red) / (float)d;
+  const float inv = 1.f / sqrtf(var + eps);
+  uint2* o = reinterpret_cast<uint2*>(out + (size_t)blockIdx.x * d);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = threadIdx.x + k * kBlock;
+    if (j < n4) {
+      const half2_t lo = {(_Float16)((v[k].x - mean) * inv), (_Float16)((v[k].y - mean) * inv)};
+      const half2_t hi = {(_Float16)((v[k].z - mean) * inv), (_Float16)((v[k].w - mean) * inv)};
+      o[j] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  }
+}
+
 __global__ __launch_bounds__(kBlock) void k_fill_zero(uint4* __restrict__ p, size_t n16) {
   const size_t stride = (size_t)gridDim.x * kBlock;
   for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
@@ -146,7 +190,16 @@ hipError_t launch_gather_rows(const void* src, void* dst, const int32_t* perm, i
 }
 
 hipError_t launch_layernorm_f16(const float* x, int B, int d, float eps, void* out, hipStream_t s) {
-  k_layernorm_f16<<<B, kBlock, 0, s>>>(x, d, eps, reinterpret_cast<_Float16*>(out));
+  _Float16* o = reinterpret_cast<_Float16*>(out);
+  const int k = (d / 4 + kBlock - 1) / kBlock;  // float4 per thread
+  const bool vec = d % 4 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)out & 7) == 0;
+  if (!vec) k_layernorm_f16<<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else if (k <= 1) k_layernorm_f16_reg<1><<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else if (k <= 2) k_layernorm_f16_reg<2><<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else if (k <= 4) k_layernorm_f16_reg<4><<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else if (k <= 8) k_layernorm_f16_reg<8><<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else if (k <= 16) k_layernorm_f16_reg<16><<<B, kBlock, 0, s>>>(x, d, eps, o);
+  else k_layernorm_f16<<<B, kBlock, 0, s>>>(x, d, eps, o);
   return hipGetLastError();
 }
 

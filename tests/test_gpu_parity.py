@@ -215,7 +215,7 @@ def test_permute_hot_first(label):
     assert torch.equal(l2, l1[:, perm.long()])
 
 
-@pytest.mark.parametrize("B,d", [(1, 8192), (4, 1000), (32, 264), (3, 5)])
+@pytest.mark.parametrize("B,d", [(1, 8192), (4, 1000), (32, 264), (3, 5), (32, 8192), (2, 12288)])
 def test_layernorm_f16(B, d):
     say("layernorm", B, d)
     g = torch.Generator().manual_seed(B + d)
@@ -223,7 +223,14 @@ def test_layernorm_f16(B, d):
     got = ps.layernorm_f16(x.to(DEV)).cpu().numpy().astype(np.float64)
     ref = oracle.layernorm(x.numpy(), 1e-5)
     ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
-    assert np.all(np.abs(got - ref) <= ulp)
+    # one fp16 ulp, plus what fp32 arithmetic cannot avoid near zero: x - mean rounds at
+    # eps32 (|x| + |mean|), divided by the row's sigma (a few roundings: factor 16).  A plain fp32
+    # two-pass LayerNorm meets this bound; one with the variance taken about zero misses it on
+    # most elements.
+    xd = x.numpy().astype(np.float64)
+    eps32 = float(np.finfo(np.float32).eps)
+    slack = 16 * eps32 * (np.abs(xd).max(axis=1) + np.abs(xd.mean(axis=1))) / np.sqrt(xd.var(axis=1) + 1e-5)
+    assert np.all(np.abs(got - ref) <= ulp + slack[:, None])
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
