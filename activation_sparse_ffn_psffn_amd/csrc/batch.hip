@@ -57,7 +57,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // an offset past every buffer: the load returns zeros
+// An offset past every buffer (the load returns zeros).  Buffers are kept below 2 GiB, so
+// kNoRow plus any in-row offset (< 2 GiB) neither wraps nor lands inside a buffer.
+constexpr uint32_t kNoRow = 0x80000000u;
+constexpr size_t kMaxBufferBytes = (size_t)0x7FFFFFFF;
 
 // Loads that are issued whatever the predicate: when it is false they read a block of zeros in
 // device memory instead.  No branch around the load and no select after it, so the compiler's
@@ -139,11 +142,14 @@ __device__ __forceinline__ int blist_len(const int32_t* count, int F) {
   return n < 0 ? 0 : (n > F ? F : n);
 }
 
-// Row splits of the down projection for a list of n neurons: the partials (S x B x d fp32) are
-// kept to about a quarter of the weight bytes the splits stream, and each split is a whole number
+// Row splits of the down projection for a list of n neurons: at least enough splits for each to
+// fit one chunk of the down kernel, more while the partials (S x B x d fp32) stay below about a
+// quarter of the weight bytes the splits stream, at most kBSplitCap; each split is a whole number
 // of 32-row steps.  S >= 1 (an empty list still writes one zero partial).
-__device__ __forceinline__ void bsplit(int n, int B, int d, int row_bytes, int& ks, int& S) {
+__device__ __forceinline__ void bsplit(int n, int B, int d, int row_bytes, int chunk_rows, int& ks, int& S) {
   long long want = (long long)n * row_bytes / ((long long)B * d * 16);
+  const long long fit = (n + chunk_rows - 1) / chunk_rows;  // splits of at most one chunk, if allowed
+  if (want < fit) want = fit;
   if (want < 1) want = 1;
   if (want > kBSplitCap) want = kBSplitCap;
   ks = (int)((n + want - 1) / want);
@@ -837,116 +843,167 @@ __global__ __launch_bounds__(kBlock) void k_bact(BArgs g, int nkc, int nbp) {
 // operands (columns x rows); the B operands are the activations of the 32 rows (hi and lo parts;
 // 4-bit: times the rows' scales of this column group).  partial[s][n][col] for n < B.
 
-template <St WT> struct BDown;
-template <> struct BDown<St::F16> { static constexpr int LPS = 4; static constexpr int D = 4; };
-template <> struct BDown<St::I4> { static constexpr int LPS = 1; static constexpr int D = 8; };  // (4 with 32 tokens)
+template <St WT, int NT> struct BDn;
+template <int NT> struct BDn<St::I4, NT> { static constexpr int LPS = 1; static constexpr int CS = NT == 1 ? 16 : 8; };
+template <int NT> struct BDn<St::F16, NT> { static constexpr int LPS = 4; static constexpr int CS = 8; };
 
 template <St WT, int NT>
-__global__ __launch_bounds__(kBlock) void k_bdown(BArgs g, int ks_cap) {
-  constexpr int LPS = BDown<WT>::LPS;
-  constexpr int D = (WT == St::I4 && NT == 2) ? 4 : BDown<WT>::D;
-  constexpr int AB = WT == St::I4 ? 2 : 1;  // activation loads per token tile: fp32 x 8, or fp16 hi (+ lo)
+__host__ __device__ constexpr int bdown_chunk_rows() { return BDn<WT, NT>::CS * 32; }
+template <St WT, int NT>
+__host__ __device__ constexpr int bdown_apitch() { return bdown_chunk_rows<WT, NT>() * 4 + 16; }
+template <St WT, int NT>
+__host__ __device__ constexpr size_t bdown_lds() {
+  return (size_t)16 * NT * bdown_apitch<WT, NT>() + (size_t)bdown_chunk_rows<WT, NT>() * 4;
+}
+
+// 8 nibbles (columns c..c+7 of one row) -> 8 fp16 in column order: each byte pair of the
+// flipped nibbles is placed under the fp16 exponent of 1024 (1024 + q + 8 exactly), then 1032 is
+// subtracted from both halves
+__device__ __forceinline__ void nib8_to_f16(uint32_t w, uint32_t (&o)[4]) {
+  const uint32_t f = w ^ 0x88888888u;
+  const uint32_t lo = f & 0x0F0F0F0Fu, hi = (f >> 4) & 0x0F0F0F0Fu;
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // bytes [lo.p, 0, hi.p, 0]: columns 2p (low half) and 2p + 1 (high half)
+    const uint32_t sel = 0x0C000C00u | (uint32_t)p | ((uint32_t)(4 + p) << 16);
+    const uint32_t v = __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+    o[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) - off);
+  }
+}
+
+template <St WT, int NT>
+__global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
+  constexpr int LPS = BDn<WT, NT>::LPS;
+  constexpr int CS = BDn<WT, NT>::CS;
+  constexpr int CR = CS * 32;
+  constexpr int NBP = 16 * NT;
+  constexpr int AP = bdown_apitch<WT, NT>();
   __shared__ __align__(16) char s_w[kBlock / kWave][32 * kDPitch];
   __shared__ __align__(16) float s_sc[kBlock / kWave][32];
-  extern __shared__ int s_idx[];
+  extern __shared__ uint4 s_dyn4[];
+  char* s_a = reinterpret_cast<char*>(s_dyn4);             // activations of the chunk, per token row
+  int* s_idx = reinterpret_cast<int*>(s_a + NBP * AP);      // neuron ids of the chunk
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
   const int d = g.d;
   const int n_list = blist_len(g.count, g.F);
   const int rowb = WT == St::I4 ? d / 2 + 2 * (d / 128) : 2 * d;
   int ks, S;
-  bsplit(n_list, g.B, d, rowb, ks, S);
+  bsplit(n_list, g.B, d, rowb, CR, ks, S);
   const int s = blockIdx.y;
   if (s >= S) return;
   const int col0 = blockIdx.x * 256 + wv * 64;
   const int k_lo = s * ks;
-  const int nrows = min(min(n_list, k_lo + ks) - k_lo, ks_cap);
-  for (int j = threadIdx.x; j < nrows; j += kBlock) {
-    const int i = g.idx[k_lo + j];
-    s_idx[j] = (unsigned)i < (unsigned)g.F ? i : -1;
-  }
-  __syncthreads();
-  const int nsteps = (nrows + 31) / 32;
+  const int nrows = min(n_list, k_lo + ks) - k_lo;
   const int srow = lane >> 1, shalf = lane & 1;  // staging: row of the step, 32-column half
   char* wbuf = s_w[wv];
-  const size_t row_stride = WT == St::I4 ? (size_t)d / 2 : (size_t)d * 2;
+  const uint32_t row_stride = WT == St::I4 ? (uint32_t)d / 2 : (uint32_t)d * 2;
   const int ng = d / 128;
-  uint4 wr[D][LPS], ah[D][NT][AB], al[D][NT];
-  float sc[D];
-  auto load_step = [&](int st, uint4(&w)[LPS], uint4(&a_hi)[NT][AB], uint4(&a_lo)[NT], float& scale) {
-    const int rr = st * 32 + srow;
-    const int ir = s_idx[rr < nrows ? rr : 0];
-    const bool ok = rr < nrows && ir >= 0;
-    const int i = ok ? ir : 0;
-    const char* wrow = reinterpret_cast<const char*>(g.w_dT) + (size_t)i * row_stride;
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-      const int c = col0 + shalf * 32 + q * 8;
-      w[q] = ld16_or0(wrow + (WT == St::I4 ? (size_t)c / 2 : (size_t)c * 2), ok && c < d, g.w_dT);
-    }
-    scale = 0.f;
-    if constexpr (WT == St::I4) {
-      const int G = col0 / 128;
-      scale = h2f(ld16b_or0(g.s_dT + (size_t)i * ng + G, ok && G < ng, g.s_dT));
-    }
-    const int kk = k_lo + st * 32 + lg * 8;  // < roundup(count, 32): zero-filled past the list
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const size_t o = (size_t)(t * 16 + li) * g.ldk + kk;
-      if constexpr (WT == St::I4) {
-        a_hi[t][0] = ldg16(g.aT + o);
-        a_hi[t][1] = ldg16(g.aT + o + 4);
-      } else {
-        a_hi[t][0] = ldg16(g.ahi + o);
-        a_lo[t] = ldg16(g.alo + o);
-      }
-    }
-  };
+  const __amdgpu_buffer_rsrc_t wr_rs = rsrc(g.w_dT, (uint32_t)((size_t)g.F * row_stride));
+  const __amdgpu_buffer_rsrc_t sc_rs = rsrc(g.s_dT, WT == St::I4 ? (uint32_t)((size_t)g.F * ng * 2) : 0u);
   f4_t acc[4][NT];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = f4_t{0.f, 0.f, 0.f, 0.f};
-  if (nsteps == 0) {
-    // empty split: the zero partial below
-  } else {
+  for (int c0 = 0; c0 < nrows; c0 += CR) {
+    const int crows = min(CR, nrows - c0);
+    const int csteps = (crows + 31) / 32;
+    if (c0 > 0) __syncthreads();  // the previous chunk's LDS reads are done
+    // the chunk's neuron ids and activations (rows < csteps * 32 <= roundup(count, 32): the
+    // activations there are zero-filled), requested together
+    {
+      constexpr int PR = WT == St::I4 ? CR / 4 : CR / 8;  // 16-byte pieces per token row (per part)
+      constexpr int PARTS = WT == St::I4 ? 1 : 2;
+      constexpr int PIECES = NBP * PR * PARTS;
+      constexpr int PPT = (PIECES + kBlock - 1) / kBlock;
+      const int live_pr = WT == St::I4 ? csteps * 8 : csteps * 4;
+      int iv[(CR + kBlock - 1) / kBlock];
 #pragma unroll
-    for (int p = 0; p < D; ++p) load_step(p < nsteps ? p : nsteps - 1, wr[p], ah[p], al[p], sc[p]);
-  }
-  // one step: stage the block in LDS, read it back transposed, 2 MFMAs per tile pair
-  auto step = [&](uint4(&w)[LPS], uint4(&a_hi)[NT][AB], uint4(&a_lo)[NT], float scale_v) {
+      for (int q = 0; q < (CR + kBlock - 1) / kBlock; ++q) {
+        const int j = threadIdx.x + q * kBlock;
+        iv[q] = j < crows ? g.idx[k_lo + c0 + j] : -1;
+      }
+      uint4 av[PPT];
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int pc = threadIdx.x + q * kBlock;
+        const int part = pc / (NBP * PR), rem = pc % (NBP * PR);
+        const int n = rem / PR, e = rem % PR;
+        const bool ok = pc < PIECES && e < live_pr;
+        const size_t kk = (size_t)k_lo + c0 + (size_t)e * (WT == St::I4 ? 4 : 8);
+        const void* src = WT == St::I4 ? static_cast<const void*>(g.aT + (size_t)n * g.ldk + kk)
+                                       : static_cast<const void*>((part == 0 ? g.ahi : g.alo) + (size_t)n * g.ldk + kk);
+        av[q] = ld16_or0(src, ok, nullptr);
+      }
+#pragma unroll
+      for (int q = 0; q < (CR + kBlock - 1) / kBlock; ++q) {
+        const int j = threadIdx.x + q * kBlock;
+        if (j < CR) s_idx[j] = (unsigned)iv[q] < (unsigned)g.F ? iv[q] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < PPT; ++q) {
+        const int pc = threadIdx.x + q * kBlock;
+        if (pc < PIECES) {
+          const int part = pc / (NBP * PR), rem = pc % (NBP * PR);
+          const int n = rem / PR, e = rem % PR;
+          *reinterpret_cast<uint4*>(s_a + n * AP + part * (CR * 2) + e * 16) = av[q];
+        }
+      }
+    }
+    __syncthreads();
+    // every weight slice of the chunk in flight at once (rows past the list read zeros)
+    uint4 wr[CS][LPS];
+    uint32_t scb[CS];
+#pragma unroll
+    for (int st = 0; st < CS; ++st) {
+      const int rr = st * 32 + srow;
+      const int i = (st < csteps && rr < crows) ? s_idx[rr] : -1;
+      const uint32_t rbase = i >= 0 ? (uint32_t)i * row_stride : kNoRow;
+#pragma unroll
+      for (int q = 0; q < LPS; ++q) {
+        const int c = col0 + shalf * 32 + q * 8;
+        const uint32_t cb = WT == St::I4 ? (uint32_t)c / 2 : (uint32_t)c * 2;
+        wr[st][q] = bld16(wr_rs, c < d ? rbase + cb : kNoRow);  // kNoRow + cb stays out of range
+      }
+      if constexpr (WT == St::I4) {
+        const int G = col0 / 128;
+        scb[st] = __builtin_amdgcn_raw_buffer_load_b16(sc_rs, (i >= 0 && G < ng) ? ((uint32_t)i * ng + G) * 2 : kNoRow,
+                                                       0, 0);
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < CS; ++st) {
+      if (st < csteps) {  // (no break: the loop must unroll so that wr[st] stays in registers)
       // stage the 32 x 64 block: row srow, columns [32 shalf, 32 shalf + 32), as fp16
       char* dst = wbuf + srow * kDPitch + shalf * 64;
       if constexpr (WT == St::I4) {
-        const uint32_t wd[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+        const uint32_t wd[4] = {wr[st][0].x, wr[st][0].y, wr[st][0].z, wr[st][0].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint32_t o4[4];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const uint32_t lo = (wd[q] >> (8 * h)) & 0xFu, hi = (wd[q] >> (8 * h + 4)) & 0xFu;
-            const half2_t v = __builtin_bit_cast(half2_t, (lo | (hi << 16)) ^ 0x64086408u) -
-                              half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
-            o4[h] = __builtin_bit_cast(uint32_t, v);
-          }
+          nib8_to_f16(wd[q], o4);
           *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(o4[0], o4[1]);
           *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(o4[2], o4[3]);
         }
-        if (shalf == 0) s_sc[wv][srow] = scale_v;
+        if (shalf == 0) s_sc[wv][srow] = h2f(scb[st]);
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(w[q].x, w[q].y);
-          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(w[q].z, w[q].w);
+          *reinterpret_cast<uint2*>(dst + q * 16) = make_uint2(wr[st][q].x, wr[st][q].y);
+          *reinterpret_cast<uint2*>(dst + q * 16 + 8) = make_uint2(wr[st][q].z, wr[st][q].w);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      // B operands: rows 8 lg .. 8 lg + 8 of the step, token li (+16 t)
       h8_t fb_hi[NT], fb_lo[NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
+        const char* arow = s_a + (t * 16 + li) * AP;
         if constexpr (WT == St::I4) {
-          const float4 a0 = __builtin_bit_cast(float4, a_hi[t][0]);
-          const float4 a1 = __builtin_bit_cast(float4, a_hi[t][1]);
+          const float4 a0 = *reinterpret_cast<const float4*>(arow + (st * 32 + lg * 8) * 4);
+          const float4 a1 = *reinterpret_cast<const float4*>(arow + (st * 32 + lg * 8) * 4 + 16);
           const float4 s0 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8]);
           const float4 s1 = *reinterpret_cast<const float4*>(&s_sc[wv][lg * 8 + 4]);
           const float pv[8] = {a0.x * s0.x, a0.y * s0.y, a0.z * s0.z, a0.w * s0.w,
@@ -959,8 +1016,8 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g, int ks_cap) {
             fb_lo[t][j] = lo;
           }
         } else {
-          fb_hi[t] = as_h8(a_hi[t][0]);
-          fb_lo[t] = as_h8(a_lo[t]);
+          fb_hi[t] = as_h8(*reinterpret_cast<const uint4*>(arow + (st * 32 + lg * 8) * 2));
+          fb_lo[t] = as_h8(*reinterpret_cast<const uint4*>(arow + CR * 2 + (st * 32 + lg * 8) * 2));
         }
       }
 #pragma unroll
@@ -977,20 +1034,9 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g, int ks_cap) {
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
-  };
-  // main groups refill each consumed slot with the step D later (clamped); the last group does not
-  int st0 = 0;
-  for (; st0 + D < nsteps; st0 += D) {
-#pragma unroll
-    for (int p = 0; p < D; ++p) {
-      step(wr[p], ah[p], al[p], sc[p]);
-      const int nx = st0 + p + D;
-      load_step(nx < nsteps ? nx : nsteps - 1, wr[p], ah[p], al[p], sc[p]);
+      }
     }
   }
-#pragma unroll
-  for (int p = 0; p < D; ++p)
-    if (st0 + p < nsteps) step(wr[p], ah[p], al[p], sc[p]);
   // D[col 16 m + 4 lg + v][token li + 16 t]
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -1007,10 +1053,10 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g, int ks_cap) {
 }
 
 // k_breduce: y[n][j] = (accumulate ? y : 0) + (b_down[j] + sum over splits in split order)
-__global__ __launch_bounds__(kBlock) void k_breduce(BArgs g, int rowb) {
+__global__ __launch_bounds__(kBlock) void k_breduce(BArgs g, int rowb, int chunk_rows) {
   const int n_list = blist_len(g.count, g.F);
   int ks, S;
-  bsplit(n_list, g.B, g.d, rowb, ks, S);
+  bsplit(n_list, g.B, g.d, rowb, chunk_rows, ks, S);
   const size_t t = (size_t)blockIdx.x * kBlock + threadIdx.x;
   if (t >= (size_t)g.B * g.d) return;
   const int col = (int)(t % g.d);
@@ -1072,7 +1118,9 @@ bool batch_supported_pred(const psffn_predictor& P, int B) {
   return B > kFusedMaxBatch && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF;
 }
 bool batch_supported_ffn(const psffn_ffn& W, int B) {
-  return B > kFusedMaxBatch && B <= 32 && (W.dt == PSFFN_F16 || W.dt == PSFFN_I4G128) && W.F <= kBatchMaxF;
+  const size_t rowb = W.dt == PSFFN_I4G128 ? (size_t)W.d / 2 : (size_t)W.d * 2;
+  return B > kFusedMaxBatch && B <= 32 && (W.dt == PSFFN_F16 || W.dt == PSFFN_I4G128) && W.F <= kBatchMaxF &&
+         (size_t)W.F * rowb <= kMaxBufferBytes;
 }
 
 static void pred_args(BArgs& g, const psffn_predictor& P, const void* x, int B, float thr, float* logits, void* ws) {
@@ -1132,16 +1180,6 @@ static void ffn_args_b(BArgs& g, const psffn_ffn& W, const void* x, int B, const
   g.nq = (W.F + 31) / 32;
 }
 
-// largest row split the down projection can take for lists of up to F neurons (bsplit: a split
-// is at most 2 B d 16 / rowb rows while it is below the cap of 16 splits, else F / 16, plus rounding)
-static int bsplit_ks_cap(int F, int B, int d, int rowb) {
-  const long long t1 = 2LL * B * d * 16 / rowb + 2;
-  long long v = t1 > F / 16 + 2 ? t1 : F / 16 + 2;
-  v = ((v + 31) & ~31LL) + 32;
-  const long long f32 = (F + 31) & ~31;
-  return (int)(v < f32 ? v : f32);
-}
-
 // LDS of the persistent logits kernel, 0 when h does not fit (then the kernel with h fragments
 // read from L2 runs instead)
 static size_t bq_lds(int nbp, int r) {
@@ -1183,7 +1221,7 @@ static hipError_t pred_launch(const BArgs& g, hipStream_t s) {
   const int nkb = (g.r + 127) / 128;
   const int nkb_t = nkb <= 4 ? 4 : (nkb <= 8 ? 8 : 12);
   const size_t lds_full = 2 * (size_t)nbp * bq_full_pitch(nkb_t);
-  if (nkb <= 12 && lds_full <= (size_t)160 * 1024 && (size_t)g.F * g.r * 2 < (size_t)0xFFFFFFF0u) {
+  if (nkb <= 12 && lds_full <= (size_t)160 * 1024 && (size_t)g.F * g.r * 2 <= kMaxBufferBytes) {
     const int tiles = (g.F + 15) / 16, per_wg = kBqFullThreads / kWave;
     int grid = cu_count();
     if (grid > (tiles + per_wg - 1) / per_wg) grid = (tiles + per_wg - 1) / per_wg;
@@ -1225,9 +1263,11 @@ static void ffn_launch_b(const BArgs& g, hipStream_t s) {
   if (act_grid > 1024) act_grid = 1024;
   k_bact<ACT><<<act_grid, kBlock, 0, s>>>(g, nkc, NBP);
   const int rowb = WT == St::I4 ? g.d / 2 + 2 * (g.d / 128) : 2 * g.d;
-  const int ks_cap = bsplit_ks_cap(g.F, g.B, g.d, rowb);
-  k_bdown<WT, NT><<<dim3((g.d + 255) / 256, kBSplitCap), kBlock, (size_t)ks_cap * 4, s>>>(g, ks_cap);
-  k_breduce<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g, rowb);
+  static_assert(bdown_lds<WT, NT>() + sizeof(char) * 4 * 32 * kDPitch + 4 * 32 * 4 <= 65536,
+                "the down kernel stays within the default 64 KB of LDS");
+  k_bdown<WT, NT><<<dim3((g.d + 255) / 256, kBSplitCap), kBlock, bdown_lds<WT, NT>(), s>>>(g);
+  k_breduce<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g, rowb,
+                                                                                       bdown_chunk_rows<WT, NT>());
 }
 
 template <St WT, psffn_act ACT>
