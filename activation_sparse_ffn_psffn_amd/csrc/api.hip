@@ -53,7 +53,8 @@ psffn_status check_ffn(const psffn_ffn* W) {
 size_t predict_scratch(int B, int r, int F) { return round256((size_t)B * r * 4) + round256((size_t)F + 16); }
 size_t compact_scratch(int F) { return round256((size_t)F + 16); }
 size_t ffn_scratch(int B, int d, int F) {
-  return round256((size_t)F * B * 4) + round256((size_t)kSplitCap * B * (size_t)d * 4);
+  const size_t splits = kUDSplitCap > kSplitCap ? kUDSplitCap : kSplitCap;
+  return round256((size_t)F * B * 4) + round256(splits * B * (size_t)d * 4);
 }
 
 // scratch of a call, whichever pipeline its batch size takes

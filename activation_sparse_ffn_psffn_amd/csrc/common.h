@@ -13,6 +13,7 @@ constexpr int kWave = 64;
 constexpr int kBlock = 256;  // 4 waves per workgroup
 constexpr int kSplitCap = 64;  // max number of k-splits of the down projection (partials buffer)
 constexpr int kSplitMinRows = 16;  // min rows per k-split
+constexpr int kUDSplitCap = 256;   // max splits of the small-batch fused up/down kernel (partials buffer)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 

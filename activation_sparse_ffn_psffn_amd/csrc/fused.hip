@@ -1,10 +1,11 @@
 // Small-batch pipeline (B <= 4), four kernels per layer:
 //
 //   k_h     h = A x                       one wave per row of A, all of a row's loads in flight
-//   k_q     l = Q h + c, threshold, and the ascending active list by decoupled look-back
-//   k_up    a_k = act(W_up[idx[k]] . x (+ gate branch))   one wave per listed neuron
-//   k_down  column tile x k-split partial sums of a_k * W_dT[idx[k]]
-//   k_reduce_splits  y = b_down + the partials summed in split order (+ y when accumulating)
+//   k_q     l = Q h + c, threshold; the ascending active list by decoupled look-back (predict
+//           call) or one mask word per 32 neurons (layer call)
+//   k_ud    per split of the list: a_k = act(W_up[idx[k]] . x (+ gate branch)), then the split's
+//           partial of sum_k a_k W_dT[idx[k]] (the layer call orders the list from the mask words)
+//   k_reduce_ud  y = b_down + the split partials summed in split order (+ y when accumulating)
 //
 // Method ("PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU", Elamur
 // Research summary): Summary 2nd paragraph (a per-layer predictor guesses the firing neurons;
@@ -13,12 +14,12 @@
 //
 // Why kernel boundaries and not in-kernel waits: measured on MI355X, a dependency resolved inside
 // a kernel costs a coherent memory round trip while every HBM queue is full (several µs), and a
-// shared counter that ~1000 workgroups touch serialises at ~7 ns per access.  A kernel boundary
-// costs ~1.5 µs.  The only in-kernel wait left is the look-back of k_q, where chunks finish
-// staggered in dispatch order and a chunk usually finds its predecessor's prefix already
-// published.
+// shared counter that ~1000 workgroups touch serialises at ~7 ns per access.  The only in-kernel
+// wait left is the look-back of k_q, where chunks finish staggered in dispatch order and a chunk
+// usually finds its predecessor's prefix already published.  The up -> down dependency stays
+// inside one workgroup of k_ud (its rows' activations never leave LDS).
 //
-// Cross-workgroup words (look-back states, tile counters, partial sums) are read and written
+// Cross-workgroup words (look-back states) are read and written
 // with relaxed device-scope atomics: on gfx950 those carry the sc1 bit, each access is coherent
 // across the XCDs' separate L2 caches on its own, and polling them costs no cache maintenance.
 // A writer waits for its data stores to complete (s_waitcnt) before bumping a counter; a reader
@@ -76,14 +77,6 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// rows per k-split of the down projection for a list of n >= 0 neurons, and the split count
-// (>= 1; an empty list still has one, empty, split so that every column tile gets reduced)
-__device__ __forceinline__ void ffn_split(int n, int& ks, int& S) {
-  ks = (n + kSplitCap - 1) / kSplitCap;
-  if (ks < 32) ks = 32;
-  S = n > 0 ? (n + ks - 1) / ks : 1;
-}
 
 constexpr int kStageX = 65536;  // bytes of LDS for the activations of all tokens (B * d * elem)
 
@@ -286,16 +279,12 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
 // =========================================================================================
 // FFN
 
-template <St WT> struct DownTile;
-template <> struct DownTile<St::F32> { static constexpr int CPL = 4; };
-template <> struct DownTile<St::F16> { static constexpr int CPL = 8; };
-template <> struct DownTile<St::I4> { static constexpr int CPL = 16; };
 
 constexpr int kMaxScanChunks = 8192;  // chunks of 32 neurons the layer path can order (F <= 262144)
 
 struct FfnArgs {
   const uint32_t* masks;  // layer path: per-chunk active bits from k_q
-  int32_t* idx_out;       // layer path: the ascending list written by k_up
+  int32_t* idx_out;       // layer path: the ascending list written by k_ud
   int32_t* count_out;
   int nq;
   size_t xbytes;
@@ -314,7 +303,6 @@ struct FfnArgs {
   float* a;
   float* part;
   uint32_t* hdr;
-  uint32_t* tile_done;
   float* y;
   int B, d, F, accumulate;
 };
@@ -335,10 +323,9 @@ __device__ __forceinline__ int list_len(const int32_t* count, int F) {
   return n < 0 ? 0 : (n > F ? F : n);
 }
 
-// k_up: a[k][b] for every listed neuron k < count (grid-stride, one wave per neuron).  The row
-// loads of the wave's first neuron go out before the workgroup stages x in LDS.
-// SCAN mode of k_up: the chunk mask words are copied to LDS with coalesced loads (all in flight),
-// then s_pre[q] = number of active neurons in chunks before q, s_pre[nq] = total.
+// List ordering from the predictor's mask words (bit b of word q: neuron 32 q + b is active): the
+// words are copied to LDS with coalesced loads (all in flight), then s_pre[q] = number of active
+// neurons in words before q, s_pre[nq] = total.
 __device__ void chunk_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t* s_mask, int* s_pre, int* s_red) {
   for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * kBlock) {
     uint32_t v[8];
@@ -387,16 +374,47 @@ __device__ __forceinline__ int list_entry(const uint32_t* s_mask, const int* s_p
   return lo * 32 + (int)__builtin_ctz(m);
 }
 
+// =========================================================================================
+// Fused up and down projection (one kernel instead of three): split s owns list positions
+// [s ks, s ks + ks).  Its waves compute the activations of those rows (one wave per row, the whole
+// row in flight, x in LDS), keep them in LDS, and the workgroup then streams the same rows of
+// W_dT into a partial output part[s][b][col].  The up -> down dependency never leaves the
+// workgroup; k_reduce_ud sums the S partials in split order.  The split depends on the list
+// length only, so the summation order (and y) is a fixed function of (idx, count, shapes).
+
+constexpr int kUDMaxRows = 1024;  // max rows of one split (F <= kUDSplitCap * kUDMaxRows)
+
+// splits: enough to spread the rows over the CUs, few enough that the partials (S x B x d fp32,
+// written then summed) stay near a quarter of the weight bytes the rows stream
+__device__ __forceinline__ void udsplit(int n, int B, int d, int stream_bytes_per_row, int& ks, int& S) {
+  long long want = (long long)n * stream_bytes_per_row / ((long long)B * d * 16);
+  if (want > kUDSplitCap) want = kUDSplitCap;
+  if (want < 1) want = 1;
+  ks = (int)((n + want - 1) / want);
+  if (ks < 1) ks = 1;
+  S = n > 0 ? (n + ks - 1) / ks : 1;
+}
+
+template <St WT>
+__host__ __device__ inline int ud_stream_bytes(int d, psffn_act act) {
+  const int rb = WT == St::F32 ? 4 * d : (WT == St::F16 ? 2 * d : d / 2 + 2 * (d / 128));
+  return (act == PSFFN_SWIGLU ? 3 : 2) * rb;
+}
+
 template <St WT, psffn_act ACT, int NB, bool SCAN>
-__global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
+__global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int XSZ = WT == St::F32 ? 4 : 2;
   constexpr int UN = ACT == PSFFN_SWIGLU ? 8 : 16;
-  extern __shared__ uint4 s_x[];  // B * d activations, then (SCAN) the chunk prefix
+  extern __shared__ uint4 s_x[];  // x (B * d), then (SCAN) the chunk prefix, then the split's rows
   __shared__ int s_red[kBlock / kWave];
-  int n;
-  uint32_t* s_mask = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s_x) + g.xbytes);
+  char* dyn = reinterpret_cast<char*>(s_x);
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(dyn + g.xbytes);
   int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
+  const size_t rows_off = g.xbytes + (SCAN ? round256(4 * (size_t)(2 * g.nq + 1)) : 0);
+  float* s_a = reinterpret_cast<float*>(dyn + rows_off);                 // [kUDMaxRows][NB]
+  int* s_i = reinterpret_cast<int*>(dyn + rows_off + 4 * (size_t)kUDMaxRows * NB);  // [kUDMaxRows]
+  int n;
   if constexpr (SCAN) {
     chunk_prefix(g.masks, g.nq, s_mask, s_pre, s_red);
     n = min(s_pre[g.nq], g.F);
@@ -404,23 +422,61 @@ __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
   } else {
     n = list_len(g.count, g.F);
   }
-  if (blockIdx.x * (kBlock / kWave) >= n) return;  // no neuron for this workgroup
-  const int lane = wave_lane();
+  int ks, S;
+  udsplit(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
+  const int s = blockIdx.x;
+  if (s >= S) return;
+  const int k_lo = s * ks, k_hi = min(n, k_lo + ks);
+  const int nr = k_hi > k_lo ? min(k_hi - k_lo, kUDMaxRows) : 0;
+  const int lane = wave_lane(), wv = wave_id();
   const size_t rb = row_bytes<WT>(g.d);
   const char* xs = reinterpret_cast<const char*>(s_x);
-  bool staged = false;
-  for (int k0 = blockIdx.x * (kBlock / kWave); k0 < n; k0 += gridDim.x * (kBlock / kWave)) {
-    const int k = k0 + wave_id();
-    int i = -1;
+  // ---- the split's neuron ids (SCAN: from the chunk prefix, and written out as the list)
+  for (int kr = threadIdx.x; kr < nr; kr += kBlock) {
+    const int k = k_lo + kr;
+    int i;
     if constexpr (SCAN) {
-      if (k < n) {
-        i = list_entry(s_mask, s_pre, g.nq, k);
-        if (lane == 0) g.idx_out[k] = i;
-      }
+      i = list_entry(s_mask, s_pre, g.nq, k);
+      g.idx_out[k] = i;
     } else {
-      i = k < n ? g.idx[k] : -1;
+      i = g.idx[k];
     }
-    const bool valid = (unsigned)i < (unsigned)g.F;
+    s_i[kr] = (unsigned)i < (unsigned)g.F ? i : -1;
+  }
+  __syncthreads();
+  // ---- the first batch of down-projection rows is requested now: it depends on the ids only,
+  // so it streams while the up rows are reduced
+  constexpr int CPL = WT == St::F32 ? 4 : (WT == St::F16 ? 8 : 32);  // columns per 16-byte slice
+  constexpr int UG = 32 / CPL;                                         // slices per group
+  constexpr int RB = 16 / UG;                                          // rows per batch
+  const int nsl = g.d / CPL;  // d % 8 == 0 (dense) or d % 128 == 0 (4-bit): whole slices
+  const int ng = g.d / 128;
+  uint4 dw[RB][UG];
+  float dsc[RB][UG];
+  auto load_down = [&](int u0, int r0) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int i = r0 + r < nr ? s_i[r0 + r] : -1;
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const int sl = u0 + u * kBlock;
+        const bool ok = i >= 0 && sl < nsl;
+        dw[r][u] = ok ? ld16(reinterpret_cast<const char*>(g.w_dT) + (size_t)i * rb + (size_t)sl * 16)
+                      : make_uint4(0, 0, 0, 0);
+        dsc[r][u] = 1.f;
+        if constexpr (WT == St::I4)
+          dsc[r][u] = ok ? h2f(reinterpret_cast<const uint16_t*>(g.s_dT)[(size_t)i * ng + sl * CPL / 128]) : 0.f;
+      }
+    }
+  };
+  if ((int)threadIdx.x < nsl) load_down(threadIdx.x, 0);
+  // ---- up: one wave per row of the split
+  bool staged = false;
+  for (int k0 = 0; k0 < nr || !staged; k0 += kBlock / kWave) {
+    const int kr = k0 + wv;  // row within the split
+    const bool live = kr < nr;
+    const int i = live ? s_i[kr] : -1;
+    const bool valid = i >= 0;
     const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)(valid ? i : 0) * rb;
     const char* grow =
         ACT == PSFFN_SWIGLU ? reinterpret_cast<const char*>(g.w_gate) + (size_t)(valid ? i : 0) * rb : nullptr;
@@ -429,7 +485,6 @@ __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
     for (int b = 0; b < NB; ++b) uacc[b] = gacc[b] = 0.f;
     uint4 wu[UN], wg[UN];
     int base = lane * EPL;
-    // loads of a batch of UN slices; lanes past the end of the row load nothing
     auto load_batch = [&]() {
 #pragma unroll
       for (int q = 0; q < UN; ++q) {
@@ -440,11 +495,11 @@ __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
       }
     };
     load_batch();
-    // every thread of the workgroup takes part in staging x (uniform: first neuron of the block)
-    if (!staged) {
+    if (!staged) {  // every thread takes part (uniform: the first pass of the loop)
       stage_x(g.x, (size_t)g.B * g.d * XSZ, s_x);
       staged = true;
     }
+    if (!live) continue;
     for (;;) {
 #pragma unroll
       for (int q = 0; q < UN; ++q) {
@@ -478,151 +533,119 @@ __global__ __launch_bounds__(kBlock) void k_up(FfnArgs g) {
         av = uu > 0.f ? uu : 0.f;
       }
       if (!valid) av = 0.f;
-      if (lane == 0 && b < g.B && k < n) g.a[(size_t)k * g.B + b] = av;
+      if (lane == 0) s_a[kr * NB + b] = b < g.B ? av : 0.f;
     }
-  }
-}
-
-// Issue the loads of PF rows k0, k0+4, ... of the list for this lane's columns: all PF indices
-// first, then all PF weight slices, so a batch costs two memory round trips, not 2*PF.
-template <St WT, int PF>
-__device__ __forceinline__ void down_batch_load(const FfnArgs& g, int k0, int k_hi, int col0, bool live,
-                                                uint4 (&wr)[PF], float (&sc)[PF], int (&rows)[PF]) {
-#pragma unroll
-  for (int p = 0; p < PF; ++p) rows[p] = k0 + 4 * p < k_hi ? g.idx[k0 + 4 * p] : -1;
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    int i = rows[p];
-    if ((unsigned)i >= (unsigned)g.F) i = -1;
-    rows[p] = i;
-    wr[p] = make_uint4(0, 0, 0, 0);
-    sc[p] = 1.f;
-    if (i >= 0 && live) {
-      if constexpr (WT == St::F32) {
-        wr[p] = ld16(reinterpret_cast<const float*>(g.w_dT) + (size_t)i * g.d + col0);
-      } else if constexpr (WT == St::F16) {
-        wr[p] = ld16(reinterpret_cast<const uint16_t*>(g.w_dT) + (size_t)i * g.d + col0);
-      } else {
-        uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(g.w_dT) + (size_t)i * (g.d / 2) +
-                                                  col0 / 2);
-        wr[p] = make_uint4(v.x, v.y, 0, 0);
-        sc[p] = group_scale<WT>(g.s_dT, i, g.d, col0);
-      }
-    }
-  }
-}
-
-constexpr int kActStage = 4096;  // floats of LDS for one split's activations (rows x batch)
-
-// k_down: workgroup (tile, s) = column tile x k-split; its 4 waves take the split's rows round
-// robin (PF rows in flight per wave) and are combined in wave order through LDS into the split's
-// partial.  (A last-arriving split reducing the tile inside this kernel was measured slower: the
-// coherent store, counter and load round trips cost ~8 us after the weights had streamed.)
-template <St WT, int NB>
-__global__ __launch_bounds__(kBlock) void k_down(FfnArgs g) {
-  constexpr int CPL = DownTile<WT>::CPL;
-  constexpr int TW = kWave * CPL;
-  constexpr int PF = 8;
-  __shared__ float s_acc[NB * TW];
-  __shared__ float s_a[kActStage];
-  const int n = list_len(g.count, g.F);
-  int ks, S;
-  ffn_split(n, ks, S);
-  const int s = blockIdx.y, tile = blockIdx.x;
-  if (s >= S) return;
-  const int lane = wave_lane(), wv = wave_id();
-  const int col0 = tile * TW + lane * CPL;
-  const bool live = col0 < g.d;
-  const int k_lo = s * ks;
-  const int k_hi = min(n, k_lo + ks);
-  uint4 wr[PF];
-  float sc[PF];
-  int rows[PF];
-  down_batch_load<WT, PF>(g, k_lo + wv, k_hi, col0, live, wr, sc, rows);
-  // the split's activations a[k_lo..k_hi) x B, 8 loads in flight per thread
-  const int na = (k_hi - k_lo) * g.B;
-  for (int q0 = threadIdx.x; q0 < na; q0 += 8 * kBlock) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = q0 + u * kBlock < na ? g.a[(size_t)k_lo * g.B + q0 + u * kBlock] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (q0 + u * kBlock < na) s_a[q0 + u * kBlock] = v[u];
   }
   __syncthreads();
-  float acc[NB][CPL];
+  // ---- down: every thread owns 16-byte column slices of W_dT; UG slices x RB rows in flight
+  for (int u0 = threadIdx.x; u0 < nsl; u0 += UG * kBlock) {
+    float acc[UG][NB][CPL];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int u = 0; u < UG; ++u)
 #pragma unroll
-    for (int e = 0; e < CPL; ++e) acc[b][e] = 0.f;
-  for (int k0 = k_lo + wv; k0 < k_hi; k0 += 4 * PF) {
-    if (k0 != k_lo + wv) down_batch_load<WT, PF>(g, k0, k_hi, col0, live, wr, sc, rows);
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int k = k0 + 4 * p;
-      if (rows[p] < 0) continue;
-      float w[CPL];
-      if constexpr (WT == St::F32) {
-        w[0] = __uint_as_float(wr[p].x); w[1] = __uint_as_float(wr[p].y);
-        w[2] = __uint_as_float(wr[p].z); w[3] = __uint_as_float(wr[p].w);
-      } else if constexpr (WT == St::F16) {
-        w[0] = h2f(wr[p].x & 0xffff); w[1] = h2f(wr[p].x >> 16); w[2] = h2f(wr[p].y & 0xffff);
-        w[3] = h2f(wr[p].y >> 16); w[4] = h2f(wr[p].z & 0xffff); w[5] = h2f(wr[p].z >> 16);
-        w[6] = h2f(wr[p].w & 0xffff); w[7] = h2f(wr[p].w >> 16);
-      } else {
+        for (int c = 0; c < CPL; ++c) acc[u][b][c] = 0.f;
+    for (int r0 = 0; r0 < nr; r0 += RB) {
+      if (u0 != (int)threadIdx.x || r0 != 0) load_down(u0, r0);  // the first batch is already in flight
+      uint4(&w)[RB][UG] = dw;
+      float(&sc)[RB][UG] = dsc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = i4_elem(wr[p].x, e) * sc[p];
+      for (int r = 0; r < RB; ++r) {
+        if (r0 + r >= nr) continue;  // (no break: the loop must unroll, w[r] stays in registers)
+        float ab[NB];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[8 + e] = i4_elem(wr[p].y, e) * sc[p];
+        for (int b = 0; b < NB; ++b) ab[b] = s_a[(r0 + r) * NB + b];
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+          float wv8[CPL];
+          if constexpr (WT == St::F32) {
+            wv8[0] = __uint_as_float(w[r][u].x); wv8[1] = __uint_as_float(w[r][u].y);
+            wv8[2] = __uint_as_float(w[r][u].z); wv8[3] = __uint_as_float(w[r][u].w);
+          } else if constexpr (WT == St::F16) {
+            const uint32_t ww[4] = {w[r][u].x, w[r][u].y, w[r][u].z, w[r][u].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              wv8[2 * h] = h2f(ww[h] & 0xffffu);
+              wv8[2 * h + 1] = h2f(ww[h] >> 16);
+            }
+          } else {
+            const uint32_t ww[4] = {w[r][u].x, w[r][u].y, w[r][u].z, w[r][u].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) wv8[8 * h + e] = i4_elem(ww[h], e) * sc[r][u];
+          }
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[u][b][c] = fmaf(ab[b], wv8[c], acc[u][b][c]);
+        }
       }
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        if (b < g.B) {
-          const float ab = s_a[(k - k_lo) * g.B + b];
-#pragma unroll
-          for (int e = 0; e < CPL; ++e) acc[b][e] = fmaf(ab, w[e], acc[b][e]);
-        }
     }
-  }
-  // combine the 4 waves in wave order through LDS; the partial goes out with plain stores (the
-  // reduce kernel reads it after the kernel boundary)
-  for (int step = 0; step < kBlock / kWave; ++step) {
-    if (wv == step) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+    for (int u = 0; u < UG; ++u) {
+      const int sl = u0 + u * kBlock;
+      if (sl >= nsl) continue;
 #pragma unroll
-        for (int e = 0; e < CPL; ++e) {
-          const int at = b * TW + lane * CPL + e;
-          const float v = step == 0 ? acc[b][e] : s_acc[at] + acc[b][e];
-          if (step < kBlock / kWave - 1)
-            s_acc[at] = v;
-          else if (live && b < g.B)
-            g.part[((size_t)s * g.B + b) * g.d + col0 + e] = v;
-        }
+      for (int b = 0; b < NB; ++b) {
+        if (b >= g.B) continue;
+        float* dst = g.part + ((size_t)s * g.B + b) * g.d + (size_t)sl * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; c += 4)
+          *reinterpret_cast<float4*>(dst + c) = make_float4(acc[u][b][c], acc[u][b][c + 1], acc[u][b][c + 2],
+                                                            acc[u][b][c + 3]);
+      }
     }
-    if (step < kBlock / kWave - 1) __syncthreads();
   }
 }
 
-// k_reduce: y[b][j] = (accumulate ? y[b][j] : 0) + (b_down[j] + sum_{s < S} part[s][b][j]), the
-// sum in split order.  One thread per output; all of its partial loads in flight at once.
-__global__ __launch_bounds__(kBlock) void k_reduce_splits(FfnArgs g) {
-  const int n = list_len(g.count, g.F);
+// y = (accumulate ? y : 0) + (b_down + the S split partials summed in split order).  Workgroup =
+// 64 consecutive outputs (16 float4); its 16 thread groups take consecutive ranges of splits, and
+// the group sums are added in group order.
+template <St WT, psffn_act ACT>
+__global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
+  __shared__ float4 s_sum[16][16];
+  const int n = list_len(g.count, g.F);  // the layer path's up kernel wrote it
   int ks, S;
-  ffn_split(n, ks, S);
-  const size_t t = (size_t)blockIdx.x * kBlock + threadIdx.x;
-  if (t >= (size_t)g.B * g.d) return;
-  const int b = (int)(t / g.d), col = (int)(t % g.d);
-  float v = g.b_down ? g.b_down[col] : 0.f;
-  for (int s0 = 0; s0 < S; s0 += 32) {
-    float pv[32];
+  udsplit(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
+  const size_t total4 = (size_t)g.B * g.d / 4;
+  const int q = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const size_t o4 = (size_t)blockIdx.x * 16 + q;
+  const int per = (S + 15) / 16;
+  const int s0 = grp * per, s1 = min(S, s0 + per);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (o4 < total4) {
+    const float4* p = reinterpret_cast<const float4*>(g.part);
+    for (int b0 = s0; b0 < s1; b0 += 8) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) pv[u] = s0 + u < S ? g.part[((size_t)(s0 + u) * g.B + b) * g.d + col] : 0.f;
+      for (int u = 0; u < 8; ++u) v[u] = b0 + u < s1 ? p[(size_t)(b0 + u) * total4 + o4] : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int u = 0; u < 32; ++u)
-      if (s0 + u < S) v += pv[u];
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < s1) {
+          acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+        }
+    }
   }
-  g.y[t] = g.accumulate ? g.y[t] + v : v;
+  s_sum[grp][q] = acc;
+  __syncthreads();
+  if (grp == 0 && o4 < total4) {
+    // y and b_down are only 4-byte aligned: scalar accesses
+    const int col = (int)((o4 * 4) % (size_t)g.d);
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+    if (g.b_down) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) t[c] = g.b_down[col + c];
+    }
+    for (int k = 0; k < 16; ++k) {
+      const float4 v = s_sum[k][q];
+      t[0] += v.x; t[1] += v.y; t[2] += v.z; t[3] += v.w;
+    }
+    float* yp = g.y + o4 * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) yp[c] = g.accumulate ? yp[c] + t[c] : t[c];
+  }
 }
 
 // =========================================================================================
@@ -677,12 +700,8 @@ hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, 
 
 template <St WT>
 static bool ffn_fits(const psffn_ffn& W, int B) {
-  // the largest split (all F neurons listed) must fit the LDS activation stage, x must fit LDS
-  int ks_max = (W.F + kSplitCap - 1) / kSplitCap;
-  if (ks_max < 32) ks_max = 32;
-  constexpr int TW = kWave * DownTile<WT>::CPL;
-  return ks_max * B <= kActStage && (W.d + TW - 1) / TW <= kMaxTiles &&
-         (size_t)B * W.d * (WT == St::F32 ? 4 : 2) <= (size_t)kStageX;
+  // every split fits the fused kernel's row capacity, x fits LDS
+  return W.F <= kUDSplitCap * kUDMaxRows && (size_t)B * W.d * (WT == St::F32 ? 4 : 2) <= (size_t)kStageX;
 }
 
 template <St WT>
@@ -706,7 +725,6 @@ static FfnArgs ffn_args(const psffn_ffn& W, const void* x, int B, const int32_t*
   g.a = reinterpret_cast<float*>(w + L.scratch);
   g.part = reinterpret_cast<float*>(w + L.scratch + round256((size_t)W.F * B * 4));
   g.hdr = reinterpret_cast<uint32_t*>(w);
-  g.tile_done = reinterpret_cast<uint32_t*>(w + L.tile_done);
   g.y = y;
   g.B = B;
   g.d = W.d;
@@ -717,15 +735,26 @@ static FfnArgs ffn_args(const psffn_ffn& W, const void* x, int B, const int32_t*
 }
 
 template <St WT, psffn_act ACT, int NB, bool SCAN>
+static size_t ud_lds(const FfnArgs& g) {
+  return g.xbytes + (SCAN ? round256(4 * (size_t)(2 * g.nq + 1)) : 0) + 4 * (size_t)kUDMaxRows * NB +
+         4 * (size_t)kUDMaxRows;
+}
+
+template <St WT, psffn_act ACT, int NB, bool SCAN>
+static hipError_t ud_attr() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_ud<WT, ACT, NB, SCAN>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+  return e;
+}
+
+template <St WT, psffn_act ACT, int NB, bool SCAN>
 static void ffn_launch(const FfnArgs& g, hipStream_t s) {
-  constexpr int TW = kWave * DownTile<WT>::CPL;
-  const int T = (g.d + TW - 1) / TW;
-  int up_grid = (g.F + 3) / 4;
-  if (up_grid > 1024) up_grid = 1024;
-  const size_t lds = g.xbytes + (SCAN ? 4 * (size_t)(2 * g.nq + 1) : 0);
-  k_up<WT, ACT, NB, SCAN><<<up_grid, kBlock, lds, s>>>(g);
-  k_down<WT, NB><<<dim3(T, kSplitCap), kBlock, 0, s>>>(g);
-  k_reduce_splits<<<(unsigned)(((size_t)g.B * g.d + kBlock - 1) / kBlock), kBlock, 0, s>>>(g);
+  const size_t lds = ud_lds<WT, ACT, NB, SCAN>(g);
+  if (lds > (size_t)64 * 1024) ud_attr<WT, ACT, NB, SCAN>();
+  int grid = kUDSplitCap;
+  if (grid > g.F) grid = g.F;
+  k_ud<WT, ACT, NB, SCAN><<<grid, kBlock, lds, s>>>(g);
+  k_reduce_ud<WT, ACT><<<(unsigned)(((size_t)g.B * g.d / 4 + 15) / 16), kBlock, 0, s>>>(g);
 }
 
 template <St WT, psffn_act ACT, int NB>
@@ -757,17 +786,19 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
   return ffn_nb<St::I4, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s);
 }
 
-// ---- one decode step of one layer: k_h, k_q (mask words only), k_up (orders the list from the
-// masks, writes idx/count, computes the activations), k_down (partials + fixed-order reduce)
+// ---- one decode step of one layer: k_h, k_q (mask words only), k_ud (orders the list from the
+// masks, writes idx/count, the activations and the down-projection partials), k_reduce_ud
 
 template <St PT, St WT, psffn_act ACT, int NB, int RV>
 static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
   constexpr int RPW = 8;
   const int NQ = (P.F + 4 * RPW - 1) / (4 * RPW);
-  // k_up's LDS: the activations plus 8 bytes per chunk must fit the default 64 KB allocation
+  // the fused up/down kernel's LDS: the activations, the chunk prefix and the split's rows
+  const size_t ud = round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2)) + round256(4 * (size_t)(2 * NQ + 1)) +
+                    4 * (size_t)kUDMaxRows * NB + 4 * (size_t)kUDMaxRows;
   if (!ffn_fits<WT>(W, B) || NQ > kMaxScanChunks || (size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX ||
-      round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2)) + 8 * (size_t)NQ + 4 > (size_t)65536)
+      ud > (size_t)150 * 1024)
     return hipErrorNotSupported;
   const StateLayout L = state_layout(P.F);
   char* w = static_cast<char*>(ws);
