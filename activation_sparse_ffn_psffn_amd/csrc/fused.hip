@@ -323,25 +323,17 @@ __device__ __forceinline__ int list_len(const int32_t* count, int F) {
   return n < 0 ? 0 : (n > F ? F : n);
 }
 
-// List ordering from the predictor's mask words (bit b of word q: neuron 32 q + b is active): the
-// words are copied to LDS with coalesced loads (all in flight), then s_pre[q] = number of active
-// neurons in words before q, s_pre[nq] = total.
-__device__ void chunk_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t* s_mask, int* s_pre, int* s_red) {
-  for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * kBlock) {
-    uint32_t v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = q0 + u * kBlock < nq ? masks[q0 + u * kBlock] : 0u;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (q0 + u * kBlock < nq) s_mask[q0 + u * kBlock] = v[u];
-  }
-  __syncthreads();
-  const int per = (nq + kBlock - 1) / kBlock;  // consecutive chunks per thread
+// The layer call orders the list from the predictor's mask words (bit b of word q: neuron 32 q + b
+// is active).  Thread t owns the consecutive words [t per, t per + per); a block scan of the
+// per-thread popcounts gives every thread its first list position and the total, and each thread
+// then emits the neuron ids of its words that fall in the workgroup's split, in ascending order.
+// s_red holds the 4 wave totals.  Returns the list length (clamped to F).
+__device__ __forceinline__ int scan_total(const uint32_t* s_mask, int nq, int F, int* s_red, int& first) {
+  const int per = (nq + kBlock - 1) / kBlock;
   const int q0 = threadIdx.x * per;
   int tot = 0;
   for (int u = 0; u < per; ++u)
     if (q0 + u < nq) tot += __popc(s_mask[q0 + u]);
-  // inclusive scan of the per-thread totals: within the wave, then across the 4 waves
   const int lane = wave_lane(), wv = wave_id();
   int inc = tot;
 #pragma unroll
@@ -351,36 +343,57 @@ __device__ void chunk_prefix(const uint32_t* __restrict__ masks, int nq, uint32_
   }
   if (lane == kWave - 1) s_red[wv] = inc;
   __syncthreads();
-  int run = inc - tot;
-  for (int w = 0; w < wv; ++w) run += s_red[w];
-  for (int u = 0; u < per; ++u)
-    if (q0 + u < nq) {
-      s_pre[q0 + u] = run;
-      run += __popc(s_mask[q0 + u]);
-    }
-  if (threadIdx.x == kBlock - 1) s_pre[nq] = run;
-  __syncthreads();
+  int run = inc - tot, n = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    if (w < wv) run += s_red[w];
+    n += s_red[w];
+  }
+  first = run;
+  return n < F ? n : F;
 }
 
-// neuron at list position k, from the chunk prefix and mask words in LDS (binary search + bit select)
-__device__ __forceinline__ int list_entry(const uint32_t* s_mask, const int* s_pre, int nq, int k) {
-  int lo = 0, hi = nq - 1;  // last chunk with s_pre[q] <= k
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
+// ids of list positions [k_lo, k_hi) owned by this thread's words -> s_i[k - k_lo] (and the list)
+__device__ __forceinline__ void scan_emit(const uint32_t* s_mask, int nq, int F, int first, int k_lo, int k_hi,
+                                          int* s_i, int32_t* idx_out) {
+  const int per = (nq + kBlock - 1) / kBlock;
+  const int q0 = threadIdx.x * per;
+  int pos = first;
+  for (int u = 0; u < per && pos < k_hi; ++u) {
+    const int q = q0 + u;
+    if (q >= nq) break;
+    uint32_t m = s_mask[q];
+    const int c = __popc(m);
+    if (pos + c <= k_lo) {
+      pos += c;
+      continue;
+    }
+    while (m != 0u && pos < k_hi) {
+      const int i = q * 32 + (int)__builtin_ctz(m);
+      m &= m - 1u;
+      if (pos >= k_lo) {
+        const bool ok = i < F;
+        s_i[pos - k_lo] = ok ? i : -1;
+        idx_out[pos] = ok ? i : 0;
+      }
+      ++pos;
+    }
   }
-  uint32_t m = s_mask[lo];
-  for (int j = k - s_pre[lo]; j > 0; --j) m &= m - 1u;  // drop the j lowest set bits
-  return lo * 32 + (int)__builtin_ctz(m);
 }
 
 // =========================================================================================
 // Fused up and down projection (one kernel instead of three): split s owns list positions
-// [s ks, s ks + ks).  Its waves compute the activations of those rows (one wave per row, the whole
-// row in flight, x in LDS), keep them in LDS, and the workgroup then streams the same rows of
-// W_dT into a partial output part[s][b][col].  The up -> down dependency never leaves the
-// workgroup; k_reduce_ud sums the S partials in split order.  The split depends on the list
-// length only, so the summation order (and y) is a fixed function of (idx, count, shapes).
+// [s ks, s ks + ks).  Its waves compute the activations of those rows (x in LDS), keep them in
+// LDS, and the workgroup then streams the same rows of W_dT into a partial output
+// part[s][b][col].  The up -> down dependency never leaves the workgroup; k_reduce_ud sums the S
+// partials in split order.  The split depends on the list length only, so the summation order
+// (and y) is a fixed function of (idx, count, shapes).
+//
+// Dense weights: one wave per up row (the whole row in flight), each thread owns 16-byte column
+// slices of W_dT.  4-bit weights (rows of d/2 bytes, several per split): 16 lanes per up row, so
+// a wave has 4 rows in flight, with the group scales requested beside the weights; in the down
+// projection each thread owns 16-column units and decodes two rows at a time into fp16 pairs that
+// feed fp32 dot2 products with (hi, lo) fp16 halves of activation x scale.
 
 constexpr int kUDMaxRows = 1024;  // max rows of one split (F <= kUDSplitCap * kUDMaxRows)
 
@@ -401,23 +414,102 @@ __host__ __device__ inline int ud_stream_bytes(int d, psffn_act act) {
   return (act == PSFFN_SWIGLU ? 3 : 2) * rb;
 }
 
+// read through this block when a lane has nothing to load (keeps every load unconditional)
+__device__ uint4 g_zero_ud[1] = {{0u, 0u, 0u, 0u}};  // never written
+
+__device__ __forceinline__ uint4 ld16z(const void* p, bool ok) {
+  return *reinterpret_cast<const uint4*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+__device__ __forceinline__ uint2 ld8z(const void* p, bool ok) {
+  return *reinterpret_cast<const uint2*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+__device__ __forceinline__ uint32_t ld2z(const void* p, bool ok) {
+  return (uint32_t)*reinterpret_cast<const uint16_t*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+
+// 4-bit decode with the sign bits pre-flipped (w ^ 0x88888888): the pair of nibbles at bits
+// [s, s+4) and [16+s, 20+s) as fp16 (1024 + q + 8) - 1032 = q, exactly
+__device__ __forceinline__ half2_t i4p(uint32_t wf, int s) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  return __builtin_bit_cast(half2_t, ((wf >> s) & 0x000F000Fu) | 0x64006400u) - off;
+}
+
+// sum of 32 products: one 16-byte slice of 4-bit weights x 32 fp16 activations stored pre-paired
+// ((x0,x4),(x1,x5),(x2,x6),(x3,x7) per 8)
+__device__ __forceinline__ float dot32_i4(uint4 w, const uint4* __restrict__ px) {
+  const uint32_t ww[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u, w.w ^ 0x88888888u};
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint4 p = px[k];
+    acc = __builtin_amdgcn_fdot2(i4p(ww[k], 0), __builtin_bit_cast(half2_t, p.x), acc, false);
+    acc = __builtin_amdgcn_fdot2(i4p(ww[k], 4), __builtin_bit_cast(half2_t, p.y), acc, false);
+    acc = __builtin_amdgcn_fdot2(i4p(ww[k], 8), __builtin_bit_cast(half2_t, p.z), acc, false);
+    acc = __builtin_amdgcn_fdot2(i4p(ww[k], 12), __builtin_bit_cast(half2_t, p.w), acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// fp32 -> (hi, lo) fp16 with hi + lo = v to ~22 bits
+__device__ __forceinline__ void split_hl16(float v, _Float16& hi, _Float16& lo) {
+  hi = (_Float16)v;
+  lo = (_Float16)(v - (float)hi);
+}
+
 template <St WT, psffn_act ACT, int NB, bool SCAN>
 __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   constexpr int EPL = Tr<WT>::EPL;
   constexpr int XSZ = WT == St::F32 ? 4 : 2;
-  constexpr int UN = ACT == PSFFN_SWIGLU ? 8 : 16;
-  extern __shared__ uint4 s_x[];  // x (B * d), then (SCAN) the chunk prefix, then the split's rows
+  constexpr int UN = ACT == PSFFN_SWIGLU ? 12 : 16;  // dense up: 16-byte slices per lane per pass
+  extern __shared__ uint4 s_x[];  // x (B * d), then (SCAN) the mask words, then the split's rows
   __shared__ int s_red[kBlock / kWave];
   char* dyn = reinterpret_cast<char*>(s_x);
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(dyn + g.xbytes);
-  int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
   const size_t rows_off = g.xbytes + (SCAN ? round256(4 * (size_t)(2 * g.nq + 1)) : 0);
   float* s_a = reinterpret_cast<float*>(dyn + rows_off);                 // [kUDMaxRows][NB]
   int* s_i = reinterpret_cast<int*>(dyn + rows_off + 4 * (size_t)kUDMaxRows * NB);  // [kUDMaxRows]
-  int n;
+  const int lane = wave_lane(), wv = wave_id();
+  // ---- x (4-bit weights: paired for the dot2 decode) and the mask words go to LDS together
+  {
+    const int n16 = (int)((size_t)g.B * g.d * XSZ / 16);
+    const uint4* src = reinterpret_cast<const uint4*>(g.x);
+    constexpr int MW = 8;
+    uint32_t mv[MW];
+    if constexpr (SCAN) {
+#pragma unroll
+      for (int u = 0; u < MW; ++u) {
+        const int q = threadIdx.x + u * kBlock;
+        mv[u] = q < g.nq ? g.masks[q] : 0u;
+      }
+    }
+    for (int k0 = threadIdx.x; k0 < n16; k0 += 8 * kBlock) {
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = k0 + u * kBlock < n16 ? src[k0 + u * kBlock] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u * kBlock < n16) s_x[k0 + u * kBlock] = WT == St::I4 ? pair_x8(v[u]) : v[u];
+    }
+    if constexpr (SCAN) {
+#pragma unroll
+      for (int u = 0; u < MW; ++u) {
+        const int q = threadIdx.x + u * kBlock;
+        if (q < g.nq) s_mask[q] = mv[u];
+      }
+      for (int q = threadIdx.x + MW * kBlock; q < g.nq; q += kBlock) s_mask[q] = g.masks[q];
+    }
+    __syncthreads();
+  }
+  // ---- the list length, this workgroup's split and its neuron ids
+  int n, first = 0;
   if constexpr (SCAN) {
-    chunk_prefix(g.masks, g.nq, s_mask, s_pre, s_red);
-    n = min(s_pre[g.nq], g.F);
+    n = scan_total(s_mask, g.nq, g.F, s_red, first);
     if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n;
   } else {
     n = list_len(g.count, g.F);
@@ -428,173 +520,359 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   if (s >= S) return;
   const int k_lo = s * ks, k_hi = min(n, k_lo + ks);
   const int nr = k_hi > k_lo ? min(k_hi - k_lo, kUDMaxRows) : 0;
-  const int lane = wave_lane(), wv = wave_id();
+  if constexpr (SCAN) {
+    scan_emit(s_mask, g.nq, g.F, first, k_lo, k_lo + nr, s_i, g.idx_out);
+  } else {
+    for (int kr = threadIdx.x; kr < nr; kr += kBlock) {
+      const int i = g.idx[k_lo + kr];
+      s_i[kr] = (unsigned)i < (unsigned)g.F ? i : -1;
+    }
+  }
+  __syncthreads();
   const size_t rb = row_bytes<WT>(g.d);
   const char* xs = reinterpret_cast<const char*>(s_x);
-  // ---- the split's neuron ids (SCAN: from the chunk prefix, and written out as the list)
-  for (int kr = threadIdx.x; kr < nr; kr += kBlock) {
-    const int k = k_lo + kr;
-    int i;
-    if constexpr (SCAN) {
-      i = list_entry(s_mask, s_pre, g.nq, k);
-      g.idx_out[k] = i;
-    } else {
-      i = g.idx[k];
-    }
-    s_i[kr] = (unsigned)i < (unsigned)g.F ? i : -1;
-  }
-  __syncthreads();
-  // ---- the first batch of down-projection rows is requested now: it depends on the ids only,
-  // so it streams while the up rows are reduced
-  constexpr int CPL = WT == St::F32 ? 4 : (WT == St::F16 ? 8 : 32);  // columns per 16-byte slice
-  constexpr int UG = 32 / CPL;                                         // slices per group
-  constexpr int RB = 16 / UG;                                          // rows per batch
-  const int nsl = g.d / CPL;  // d % 8 == 0 (dense) or d % 128 == 0 (4-bit): whole slices
-  const int ng = g.d / 128;
-  uint4 dw[RB][UG];
-  float dsc[RB][UG];
-  auto load_down = [&](int u0, int r0) {
+  if constexpr (WT == St::I4) {
+    // ================= 4-bit weights
+    const int ng = g.d / 128;
+    const size_t srow = (size_t)ng * 2;  // bytes of one row's scales
+    // ---- down: thread t owns 16-column units t + j kBlock (j < UJ) per pass; RBD rows per batch
+    constexpr int UJ = NB == 1 ? 3 : 1;
+    constexpr int RBD = 8;
+    const int nu = g.d / 16;
+    const char* wd = reinterpret_cast<const char*>(g.w_dT);
+    const char* sd = reinterpret_cast<const char*>(g.s_dT);
+    uint2 dw[RBD][UJ];
+    uint32_t dsc[RBD][UJ];
+    auto load_down = [&](int j0, int r0) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int i = r0 + r < nr ? s_i[r0 + r] : -1;
+      for (int r = 0; r < RBD; ++r) {
+        const int i = r0 + r < nr ? s_i[r0 + r] : -1;
 #pragma unroll
-      for (int u = 0; u < UG; ++u) {
-        const int sl = u0 + u * kBlock;
-        const bool ok = i >= 0 && sl < nsl;
-        dw[r][u] = ok ? ld16(reinterpret_cast<const char*>(g.w_dT) + (size_t)i * rb + (size_t)sl * 16)
-                      : make_uint4(0, 0, 0, 0);
-        dsc[r][u] = 1.f;
-        if constexpr (WT == St::I4)
-          dsc[r][u] = ok ? h2f(reinterpret_cast<const uint16_t*>(g.s_dT)[(size_t)i * ng + sl * CPL / 128]) : 0.f;
-      }
-    }
-  };
-  if ((int)threadIdx.x < nsl) load_down(threadIdx.x, 0);
-  // ---- up: one wave per row of the split
-  bool staged = false;
-  for (int k0 = 0; k0 < nr || !staged; k0 += kBlock / kWave) {
-    const int kr = k0 + wv;  // row within the split
-    const bool live = kr < nr;
-    const int i = live ? s_i[kr] : -1;
-    const bool valid = i >= 0;
-    const char* urow = reinterpret_cast<const char*>(g.w_up) + (size_t)(valid ? i : 0) * rb;
-    const char* grow =
-        ACT == PSFFN_SWIGLU ? reinterpret_cast<const char*>(g.w_gate) + (size_t)(valid ? i : 0) * rb : nullptr;
-    float uacc[NB], gacc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) uacc[b] = gacc[b] = 0.f;
-    uint4 wu[UN], wg[UN];
-    int base = lane * EPL;
-    auto load_batch = [&]() {
-#pragma unroll
-      for (int q = 0; q < UN; ++q) {
-        const int e = base + q * kWave * EPL;
-        const size_t off = WT == St::I4 ? (size_t)e / 2 : (size_t)e * Tr<WT>::ESZ;
-        wu[q] = (valid && e < g.d) ? ld16(urow + off) : make_uint4(0, 0, 0, 0);
-        if constexpr (ACT == PSFFN_SWIGLU) wg[q] = (valid && e < g.d) ? ld16(grow + off) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < UJ; ++j) {
+          const int un = j0 + (int)threadIdx.x + j * kBlock;
+          const bool ok = i >= 0 && un < nu;
+          dw[r][j] = ld8z(wd + (size_t)(ok ? i : 0) * rb + (size_t)un * 8, ok);
+          dsc[r][j] = ld2z(sd + (size_t)(ok ? i : 0) * srow + (size_t)(un / 8) * 2, ok);
+        }
       }
     };
-    load_batch();
-    if (!staged) {  // every thread takes part (uniform: the first pass of the loop)
-      stage_x(g.x, (size_t)g.B * g.d * XSZ, s_x);
-      staged = true;
-    }
-    if (!live) continue;
-    for (;;) {
+    // ---- up: 16 lanes per row, 4 rows per wave, UQ 16-byte slices per lane per pass
+    constexpr int UQ = ACT == PSFFN_SWIGLU ? 12 : 24;
+    const int li = lane & 15, lg = lane >> 4;
+    const int step = UQ * 16 * 32;
+    const char* su_base = reinterpret_cast<const char*>(g.s_up);
+    const char* sg_base = reinterpret_cast<const char*>(g.s_gate);
+    uint4 wu[UQ], wg[UQ];
+    uint32_t su[UQ], sg[UQ];
+    float uacc[NB], gacc[NB];
+    int i = -1;
+    size_t ro = 0, so = 0;
+    auto row_begin = [&](int k0) {
+      const int kr = k0 + wv * 4 + lg;
+      i = kr < nr ? s_i[kr] : -1;
+      ro = (size_t)(i >= 0 ? i : 0) * rb;
+      so = (size_t)(i >= 0 ? i : 0) * srow;
 #pragma unroll
-      for (int q = 0; q < UN; ++q) {
-        const int e = base + q * kWave * EPL;
-        if (valid && e < g.d) {
-          const float su = group_scale<WT>(g.s_up, i, g.d, e);
-          float sg = 1.f;
-          if constexpr (ACT == PSFFN_SWIGLU) sg = group_scale<WT>(g.s_gate, i, g.d, e);
+      for (int b = 0; b < NB; ++b) uacc[b] = gacc[b] = 0.f;
+    };
+    auto up_load = [&](int e0) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-            if (b < g.B) {
-              const char* xr = xs + (size_t)b * g.d * XSZ;
-              uacc[b] = dot16<WT>(wu[q], xr, e, su, uacc[b]);
-              if constexpr (ACT == PSFFN_SWIGLU) gacc[b] = dot16<WT>(wg[q], xr, e, sg, gacc[b]);
-            }
+      for (int q = 0; q < UQ; ++q) {
+        const int e = e0 + (q * 16 + li) * 32;
+        const bool ok = i >= 0 && e < g.d;
+        wu[q] = ld16z(reinterpret_cast<const char*>(g.w_up) + ro + e / 2, ok);
+        su[q] = ld2z(su_base + so + (size_t)(e / 128) * 2, ok);
+        if constexpr (ACT == PSFFN_SWIGLU) {
+          wg[q] = ld16z(reinterpret_cast<const char*>(g.w_gate) + ro + e / 2, ok);
+          sg[q] = ld2z(sg_base + so + (size_t)(e / 128) * 2, ok);
         }
       }
-      base += UN * kWave * EPL;
-      if (base >= g.d) break;
-      load_batch();
-    }
-    const float bu = (valid && g.b_up) ? g.b_up[i] : 0.f;
-    const float bg = (valid && g.b_gate) ? g.b_gate[i] : 0.f;
+    };
+    auto up_acc = [&](int e0) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float uu = wave_sum(uacc[b]) + bu;
-      float av;
-      if constexpr (ACT == PSFFN_SWIGLU) {
-        av = silu_f(wave_sum(gacc[b]) + bg) * uu;
-      } else {
-        av = uu > 0.f ? uu : 0.f;
-      }
-      if (!valid) av = 0.f;
-      if (lane == 0) s_a[kr * NB + b] = b < g.B ? av : 0.f;
-    }
-  }
-  __syncthreads();
-  // ---- down: every thread owns 16-byte column slices of W_dT; UG slices x RB rows in flight
-  for (int u0 = threadIdx.x; u0 < nsl; u0 += UG * kBlock) {
-    float acc[UG][NB][CPL];
+      for (int q = 0; q < UQ; ++q) {
+        const int e = e0 + (q * 16 + li) * 32;
+        const int ec = e < g.d ? e : 0;  // (the weights and scales past d are zero)
 #pragma unroll
-    for (int u = 0; u < UG; ++u)
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[u][b][c] = 0.f;
-    for (int r0 = 0; r0 < nr; r0 += RB) {
-      if (u0 != (int)threadIdx.x || r0 != 0) load_down(u0, r0);  // the first batch is already in flight
-      uint4(&w)[RB][UG] = dw;
-      float(&sc)[RB][UG] = dsc;
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (r0 + r >= nr) continue;  // (no break: the loop must unroll, w[r] stays in registers)
-        float ab[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) ab[b] = s_a[(r0 + r) * NB + b];
-#pragma unroll
-        for (int u = 0; u < UG; ++u) {
-          float wv8[CPL];
-          if constexpr (WT == St::F32) {
-            wv8[0] = __uint_as_float(w[r][u].x); wv8[1] = __uint_as_float(w[r][u].y);
-            wv8[2] = __uint_as_float(w[r][u].z); wv8[3] = __uint_as_float(w[r][u].w);
-          } else if constexpr (WT == St::F16) {
-            const uint32_t ww[4] = {w[r][u].x, w[r][u].y, w[r][u].z, w[r][u].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              wv8[2 * h] = h2f(ww[h] & 0xffffu);
-              wv8[2 * h + 1] = h2f(ww[h] >> 16);
-            }
-          } else {
-            const uint32_t ww[4] = {w[r][u].x, w[r][u].y, w[r][u].z, w[r][u].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) wv8[8 * h + e] = i4_elem(ww[h], e) * sc[r][u];
+        for (int b = 0; b < NB; ++b)
+          if (b < g.B) {
+            const uint4* px = reinterpret_cast<const uint4*>(xs + ((size_t)b * g.d + ec) * 2);
+            uacc[b] = fmaf(h2f(su[q]), dot32_i4(wu[q], px), uacc[b]);
+            if constexpr (ACT == PSFFN_SWIGLU) gacc[b] = fmaf(h2f(sg[q]), dot32_i4(wg[q], px), gacc[b]);
           }
-#pragma unroll
-          for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[u][b][c] = fmaf(ab[b], wv8[c], acc[u][b][c]);
-        }
       }
-    }
-#pragma unroll
-    for (int u = 0; u < UG; ++u) {
-      const int sl = u0 + u * kBlock;
-      if (sl >= nsl) continue;
+    };
+    auto row_end = [&](int k0) {
+      const int kr = k0 + wv * 4 + lg;
+      const bool valid = i >= 0;
+      const float bu = (valid && g.b_up) ? g.b_up[i] : 0.f;
+      const float bg = (valid && g.b_gate) ? g.b_gate[i] : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        if (b >= g.B) continue;
-        float* dst = g.part + ((size_t)s * g.B + b) * g.d + (size_t)sl * CPL;
+        const float uu = sum16(uacc[b]) + bu;
+        float av;
+        if constexpr (ACT == PSFFN_SWIGLU) {
+          av = silu_f(sum16(gacc[b]) + bg) * uu;
+        } else {
+          av = uu > 0.f ? uu : 0.f;
+        }
+        if (!valid || b >= g.B) av = 0.f;
+        if (li == 0 && kr < nr) s_a[kr * NB + b] = av;
+      }
+    };
+    // the first rows' first pass goes out before the first down batch, which then streams while
+    // the up rows are reduced
+    row_begin(0);
+    up_load(0);
+    load_down(0, 0);
+    up_acc(0);
+    for (int e0 = step; e0 < g.d; e0 += step) {
+      up_load(e0);
+      up_acc(e0);
+    }
+    row_end(0);
+    for (int k0 = 4 * (kBlock / kWave); k0 < nr; k0 += 4 * (kBlock / kWave)) {
+      row_begin(k0);
+      for (int e0 = 0; e0 < g.d; e0 += step) {
+        up_load(e0);
+        up_acc(e0);
+      }
+      row_end(k0);
+    }
+    __syncthreads();
+    // ---- down: two rows at a time, y[c] += (q_r, q_r') . (hi, hi') + (q_r, q_r') . (lo, lo')
+    for (int j0 = 0; j0 < nu; j0 += UJ * kBlock) {
+      if (j0 > 0) load_down(j0, 0);
+      float acc[UJ][NB][16];
 #pragma unroll
-        for (int c = 0; c < CPL; c += 4)
-          *reinterpret_cast<float4*>(dst + c) = make_float4(acc[u][b][c], acc[u][b][c + 1], acc[u][b][c + 2],
-                                                            acc[u][b][c + 3]);
+      for (int j = 0; j < UJ; ++j)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) acc[j][b][c] = 0.f;
+      for (int r0 = 0; r0 < nr; r0 += RBD) {
+        uint2 w[RBD][UJ];
+        uint32_t sc[RBD][UJ];
+#pragma unroll
+        for (int r = 0; r < RBD; ++r)
+#pragma unroll
+          for (int j = 0; j < UJ; ++j) {
+            w[r][j] = dw[r][j];
+            sc[r][j] = dsc[r][j];
+          }
+        load_down(j0, r0 + RBD);  // the next batch (past the list: the zero block)
+#pragma unroll
+        for (int p = 0; p < RBD / 2; ++p) {
+          const int r = r0 + 2 * p;
+          if (r >= nr) continue;  // (no break: the loop must unroll, w[] stays in registers)
+          float a0[NB], a1[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            a0[b] = s_a[r * NB + b];
+            a1[b] = r + 1 < nr ? s_a[(r + 1) * NB + b] : 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < UJ; ++j) {
+            half2_t hp[NB], lp[NB];
+            const float s0 = h2f(sc[2 * p][j]), s1 = h2f(sc[2 * p + 1][j]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              _Float16 h0, l0, h1, l1;
+              split_hl16(a0[b] * s0, h0, l0);
+              split_hl16(a1[b] * s1, h1, l1);
+              hp[b] = half2_t{h0, h1};
+              lp[b] = half2_t{l0, l1};
+            }
+            const uint32_t x0[2] = {w[2 * p][j].x ^ 0x88888888u, w[2 * p][j].y ^ 0x88888888u};
+            const uint32_t x1[2] = {w[2 * p + 1][j].x ^ 0x88888888u, w[2 * p + 1][j].y ^ 0x88888888u};
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                // byte jj of both rows: columns 8h + 2jj (low nibbles) and 8h + 2jj + 1 (high)
+                const uint32_t t = __builtin_amdgcn_perm(x1[h], x0[h], 0x0C000C00u | (uint32_t)jj | ((4u + jj) << 16));
+                const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+                const half2_t vlo = __builtin_bit_cast(half2_t, (t & 0x000F000Fu) | 0x64006400u) - off;
+                const half2_t vhi = __builtin_bit_cast(half2_t, ((t >> 4) & 0x000F000Fu) | 0x64006400u) - off;
+                const int c = 8 * h + 2 * jj;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                  acc[j][b][c] = __builtin_amdgcn_fdot2(vlo, hp[b], acc[j][b][c], false);
+                  acc[j][b][c] = __builtin_amdgcn_fdot2(vlo, lp[b], acc[j][b][c], false);
+                  acc[j][b][c + 1] = __builtin_amdgcn_fdot2(vhi, hp[b], acc[j][b][c + 1], false);
+                  acc[j][b][c + 1] = __builtin_amdgcn_fdot2(vhi, lp[b], acc[j][b][c + 1], false);
+                }
+              }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < UJ; ++j) {
+        const int un = j0 + (int)threadIdx.x + j * kBlock;
+        if (un >= nu) continue;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b >= g.B) continue;
+          float* dst = g.part + ((size_t)s * g.B + b) * g.d + (size_t)un * 16;
+#pragma unroll
+          for (int c = 0; c < 16; c += 4)
+            *reinterpret_cast<float4*>(dst + c) =
+                make_float4(acc[j][b][c], acc[j][b][c + 1], acc[j][b][c + 2], acc[j][b][c + 3]);
+        }
+      }
+    }
+    return;
+  } else {
+    // ================= dense weights
+    constexpr int CPL = WT == St::F32 ? 4 : 8;  // columns per 16-byte slice
+    constexpr int UG = 32 / CPL;                // slices per thread per pass
+    constexpr int RB = 16 / UG;                 // rows per batch
+    const int nsl = g.d / CPL;                  // d % 8 == 0: whole slices
+    const char* wd = reinterpret_cast<const char*>(g.w_dT);
+    uint4 dw[RB][UG];
+    auto load_down = [&](int j0, int r0) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int i = r0 + r < nr ? s_i[r0 + r] : -1;
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+          const int sl = j0 + (int)threadIdx.x + u * kBlock;
+          const bool ok = i >= 0 && sl < nsl;
+          dw[r][u] = ld16z(wd + (size_t)(ok ? i : 0) * rb + (size_t)sl * 16, ok);
+        }
+      }
+    };
+    // ---- up: one wave per row of the split, UN 16-byte slices per lane per pass
+    const int step = UN * kWave * EPL;
+    uint4 wu[UN], wg[UN];
+    float uacc[NB], gacc[NB];
+    int i = -1;
+    size_t ro = 0;
+    auto row_begin = [&](int kr) {
+      i = kr < nr ? s_i[kr] : -1;
+      ro = (size_t)(i >= 0 ? i : 0) * rb;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) uacc[b] = gacc[b] = 0.f;
+    };
+    auto up_load = [&](int e0) {
+#pragma unroll
+      for (int q = 0; q < UN; ++q) {
+        const int e = e0 + (q * kWave + lane) * EPL;
+        const bool ok = i >= 0 && e < g.d;
+        const size_t off = ro + (size_t)e * Tr<WT>::ESZ;
+        wu[q] = ld16z(reinterpret_cast<const char*>(g.w_up) + off, ok);
+        if constexpr (ACT == PSFFN_SWIGLU) wg[q] = ld16z(reinterpret_cast<const char*>(g.w_gate) + off, ok);
+      }
+    };
+    auto up_acc = [&](int e0) {
+#pragma unroll
+      for (int q = 0; q < UN; ++q) {
+        const int e = e0 + (q * kWave + lane) * EPL;
+        const int ec = e < g.d ? e : 0;  // (the weights past d are zero)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          if (b < g.B) {
+            const char* xr = xs + (size_t)b * g.d * XSZ;
+            uacc[b] = dot16<WT>(wu[q], xr, ec, 1.f, uacc[b]);
+            if constexpr (ACT == PSFFN_SWIGLU) gacc[b] = dot16<WT>(wg[q], xr, ec, 1.f, gacc[b]);
+          }
+      }
+    };
+    auto row_end = [&](int kr) {
+      const bool valid = i >= 0;
+      const float bu = (valid && g.b_up) ? g.b_up[i] : 0.f;
+      const float bg = (valid && g.b_gate) ? g.b_gate[i] : 0.f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float uu = wave_sum(uacc[b]) + bu;
+        float av;
+        if constexpr (ACT == PSFFN_SWIGLU) {
+          av = silu_f(wave_sum(gacc[b]) + bg) * uu;
+        } else {
+          av = uu > 0.f ? uu : 0.f;
+        }
+        if (!valid || b >= g.B) av = 0.f;
+        if (lane == 0 && kr < nr) s_a[kr * NB + b] = av;
+      }
+    };
+    // the first row's first pass goes out before the first down batch, which then streams while
+    // the up rows are reduced
+    row_begin(wv);
+    up_load(0);
+    load_down(0, 0);
+    up_acc(0);
+    for (int e0 = step; e0 < g.d; e0 += step) {
+      up_load(e0);
+      up_acc(e0);
+    }
+    row_end(wv);
+    for (int k0 = kBlock / kWave; k0 < nr; k0 += kBlock / kWave) {
+      row_begin(k0 + wv);
+      for (int e0 = 0; e0 < g.d; e0 += step) {
+        up_load(e0);
+        up_acc(e0);
+      }
+      row_end(k0 + wv);
+    }
+    __syncthreads();
+    // ---- down: thread t owns 16-byte column slices t + u kBlock; the next batch of RB rows is
+    // requested before the current one is accumulated
+    for (int j0 = 0; j0 < nsl; j0 += UG * kBlock) {
+      if (j0 > 0) load_down(j0, 0);
+      float acc[UG][NB][CPL];
+#pragma unroll
+      for (int u = 0; u < UG; ++u)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[u][b][c] = 0.f;
+      for (int r0 = 0; r0 < nr; r0 += RB) {
+        uint4 w[RB][UG];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+          for (int u = 0; u < UG; ++u) w[r][u] = dw[r][u];
+        load_down(j0, r0 + RB);  // (past the list: the zero block)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          if (r0 + r >= nr) continue;  // (no break: the loop must unroll, w[r] stays in registers)
+          float ab[NB];
+#pragma unroll
+          for (int b = 0; b < NB; ++b) ab[b] = s_a[(r0 + r) * NB + b];
+#pragma unroll
+          for (int u = 0; u < UG; ++u) {
+            float wv8[CPL];
+            if constexpr (WT == St::F32) {
+              wv8[0] = __uint_as_float(w[r][u].x); wv8[1] = __uint_as_float(w[r][u].y);
+              wv8[2] = __uint_as_float(w[r][u].z); wv8[3] = __uint_as_float(w[r][u].w);
+            } else {
+              const uint32_t ww[4] = {w[r][u].x, w[r][u].y, w[r][u].z, w[r][u].w};
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                wv8[2 * h] = h2f(ww[h] & 0xffffu);
+                wv8[2 * h + 1] = h2f(ww[h] >> 16);
+              }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) acc[u][b][c] = fmaf(ab[b], wv8[c], acc[u][b][c]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UG; ++u) {
+        const int sl = j0 + (int)threadIdx.x + u * kBlock;
+        if (sl >= nsl) continue;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b >= g.B) continue;
+          float* dst = g.part + ((size_t)s * g.B + b) * g.d + (size_t)sl * CPL;
+#pragma unroll
+          for (int c = 0; c < CPL; c += 4)
+            *reinterpret_cast<float4*>(dst + c) = make_float4(acc[u][b][c], acc[u][b][c + 1], acc[u][b][c + 2],
+                                                              acc[u][b][c + 3]);
+        }
       }
     }
   }
@@ -748,21 +1026,24 @@ static hipError_t ud_attr() {
 }
 
 template <St WT, psffn_act ACT, int NB, bool SCAN>
-static void ffn_launch(const FfnArgs& g, hipStream_t s) {
+static hipError_t ffn_launch(const FfnArgs& g, hipStream_t s) {
   const size_t lds = ud_lds<WT, ACT, NB, SCAN>(g);
-  if (lds > (size_t)64 * 1024) ud_attr<WT, ACT, NB, SCAN>();
+  if (lds > (size_t)64 * 1024) {
+    const hipError_t e = ud_attr<WT, ACT, NB, SCAN>();
+    if (e != hipSuccess) return e;
+  }
   int grid = kUDSplitCap;
   if (grid > g.F) grid = g.F;
   k_ud<WT, ACT, NB, SCAN><<<grid, kBlock, lds, s>>>(g);
   k_reduce_ud<WT, ACT><<<(unsigned)(((size_t)g.B * g.d / 4 + 15) / 16), kBlock, 0, s>>>(g);
+  return hipGetLastError();
 }
 
 template <St WT, psffn_act ACT, int NB>
 static hipError_t ffn_t(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count, float* y,
                         int accumulate, void* ws, hipStream_t s) {
   if (!ffn_fits<WT>(W, B)) return hipErrorNotSupported;
-  ffn_launch<WT, ACT, NB, false>(ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws), s);
-  return hipGetLastError();
+  return ffn_launch<WT, ACT, NB, false>(ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws), s);
 }
 
 template <St WT, psffn_act ACT>
@@ -814,8 +1095,7 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   g.nq = NQ;
   g.idx_out = idx;
   g.count_out = count;
-  ffn_launch<WT, ACT, NB, true>(g, s);
-  return hipGetLastError();
+  return ffn_launch<WT, ACT, NB, true>(g, s);
 }
 
 template <St PT, St WT, psffn_act ACT, int NB>
