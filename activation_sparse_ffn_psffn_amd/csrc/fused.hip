@@ -229,9 +229,20 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
   if (lane == 0) s_mask[wv] = mask;
   __syncthreads();
   if constexpr (MASKS) {
-    // layer path: publish the chunk's active bits only; the up kernel orders them
-    static_assert(4 * RPW == 32, "one 32-bit mask word per chunk");
-    if (threadIdx.x == 0) masks[q] = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
+    // layer path: publish the chunk's active bits only; the up kernel orders them.  Chunks of 16
+    // neurons write the halves of the 32-bit words (little endian); an odd last chunk writes its
+    // whole word, so the unused upper half reads as zero.
+    static_assert(4 * RPW == 32 || 4 * RPW == 16, "chunks of 32 or 16 neurons");
+    if (threadIdx.x == 0) {
+      const uint32_t bits = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
+      if constexpr (4 * RPW == 32) {
+        masks[q] = bits;
+      } else if ((q & 1) == 0 && q == NQ - 1) {
+        masks[q >> 1] = bits;
+      } else {
+        reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
+      }
+    }
     return;
   }
   int cnt = 0;
@@ -353,32 +364,35 @@ __device__ __forceinline__ int scan_total(const uint32_t* s_mask, int nq, int F,
   return n < F ? n : F;
 }
 
-// ids of list positions [k_lo, k_hi) owned by this thread's words -> s_i[k - k_lo] (and the list)
+// ids of list positions [k_lo, k_hi) -> s_i[k - k_lo].  Each thread lists its words that
+// intersect the range (word index and first position, packed as pos << 13 | q: q < 8192,
+// pos <= 2^18) in s_wl; then lane j of a wave tests bit j of a listed word, so no thread walks
+// bits one at a time.  *s_wn must be zero on entry; both passes end with a barrier.
 __device__ __forceinline__ void scan_emit(const uint32_t* s_mask, int nq, int F, int first, int k_lo, int k_hi,
-                                          int* s_i, int32_t* idx_out) {
+                                          int* s_i, uint32_t* s_wl, int* s_wn) {
   const int per = (nq + kBlock - 1) / kBlock;
   const int q0 = threadIdx.x * per;
   int pos = first;
-  for (int u = 0; u < per && pos < k_hi; ++u) {
+  for (int u = 0; u < per; ++u) {
     const int q = q0 + u;
-    if (q >= nq) break;
-    uint32_t m = s_mask[q];
-    const int c = __popc(m);
-    if (pos + c <= k_lo) {
-      pos += c;
-      continue;
-    }
-    while (m != 0u && pos < k_hi) {
-      const int i = q * 32 + (int)__builtin_ctz(m);
-      m &= m - 1u;
-      if (pos >= k_lo) {
-        const bool ok = i < F;
-        s_i[pos - k_lo] = ok ? i : -1;
-        idx_out[pos] = ok ? i : 0;
-      }
-      ++pos;
+    const int c = q < nq ? __popc(s_mask[q]) : 0;
+    if (c > 0 && pos < k_hi && pos + c > k_lo) s_wl[atomicAdd(s_wn, 1)] = ((uint32_t)pos << 13) | (uint32_t)q;
+    pos += c;
+  }
+  __syncthreads();
+  const int nw = *s_wn;
+  const int lane = wave_lane();
+  for (int j = wave_id(); j < nw; j += kBlock / kWave) {
+    const uint32_t e = s_wl[j];
+    const int q = (int)(e & 8191u), p0 = (int)(e >> 13);
+    const uint32_t m = s_mask[q];
+    if (lane < 32 && ((m >> lane) & 1u)) {
+      const int at = p0 + __popc(m & ((1u << lane) - 1u));
+      const int i = q * 32 + lane;
+      if (at >= k_lo && at < k_hi) s_i[at - k_lo] = i < F ? i : -1;
     }
   }
+  __syncthreads();
 }
 
 // =========================================================================================
@@ -390,17 +404,20 @@ __device__ __forceinline__ void scan_emit(const uint32_t* s_mask, int nq, int F,
 // (and y) is a fixed function of (idx, count, shapes).
 //
 // Dense weights: one wave per up row (the whole row in flight), each thread owns 16-byte column
-// slices of W_dT.  4-bit weights (rows of d/2 bytes, several per split): 16 lanes per up row, so
-// a wave has 4 rows in flight, with the group scales requested beside the weights; in the down
+// slices of W_dT.  4-bit weights (rows of d/2 bytes, several per split): 32 lanes per up row, so
+// a wave has 2 rows in flight, with the group scales requested beside the weights; in the down
 // projection each thread owns 16-column units and decodes two rows at a time into fp16 pairs that
 // feed fp32 dot2 products with (hi, lo) fp16 halves of activation x scale.
 
 constexpr int kUDMaxRows = 1024;  // max rows of one split (F <= kUDSplitCap * kUDMaxRows)
 
 // splits: enough to spread the rows over the CUs, few enough that the partials (S x B x d fp32,
-// written then summed) stay near a quarter of the weight bytes the rows stream
+// written then summed) stay near a quarter of the weight bytes the rows stream (half for 4-bit
+// rows, whose decode is arithmetic-bound and wants the work spread over more CUs)
+template <St WT>
 __device__ __forceinline__ void udsplit(int n, int B, int d, int stream_bytes_per_row, int& ks, int& S) {
-  long long want = (long long)n * stream_bytes_per_row / ((long long)B * d * 16);
+  constexpr int kDiv = WT == St::I4 ? 8 : 16;
+  long long want = (long long)n * stream_bytes_per_row / ((long long)B * d * kDiv);
   if (want > kUDSplitCap) want = kUDSplitCap;
   if (want < 1) want = 1;
   ks = (int)((n + want - 1) / want);
@@ -450,9 +467,9 @@ __device__ __forceinline__ float dot32_i4(uint4 w, const uint4* __restrict__ px)
   return acc;
 }
 
-__device__ __forceinline__ float sum16(float v) {
+__device__ __forceinline__ float sum32(float v) {
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  for (int o = 16; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
@@ -469,6 +486,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   constexpr int UN = ACT == PSFFN_SWIGLU ? 12 : 16;  // dense up: 16-byte slices per lane per pass
   extern __shared__ uint4 s_x[];  // x (B * d), then (SCAN) the mask words, then the split's rows
   __shared__ int s_red[kBlock / kWave];
+  __shared__ int s_wn;
   char* dyn = reinterpret_cast<char*>(s_x);
   uint32_t* s_mask = reinterpret_cast<uint32_t*>(dyn + g.xbytes);
   const size_t rows_off = g.xbytes + (SCAN ? round256(4 * (size_t)(2 * g.nq + 1)) : 0);
@@ -479,6 +497,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   {
     const int n16 = (int)((size_t)g.B * g.d * XSZ / 16);
     const uint4* src = reinterpret_cast<const uint4*>(g.x);
+    if (threadIdx.x == 0) s_wn = 0;
     constexpr int MW = 8;
     uint32_t mv[MW];
     if constexpr (SCAN) {
@@ -510,27 +529,37 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
   int n, first = 0;
   if constexpr (SCAN) {
     n = scan_total(s_mask, g.nq, g.F, s_red, first);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n;
   } else {
     n = list_len(g.count, g.F);
   }
   int ks, S;
-  udsplit(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
+  udsplit<WT>(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
   const int s = blockIdx.x;
   if (s >= S) return;
   const int k_lo = s * ks, k_hi = min(n, k_lo + ks);
   const int nr = k_hi > k_lo ? min(k_hi - k_lo, kUDMaxRows) : 0;
   if constexpr (SCAN) {
-    scan_emit(s_mask, g.nq, g.F, first, k_lo, k_lo + nr, s_i, g.idx_out);
+    // (s_a holds the word list until the up projection writes it: kUDMaxRows entries)
+    scan_emit(s_mask, g.nq, g.F, first, k_lo, k_lo + nr, s_i, reinterpret_cast<uint32_t*>(s_a), &s_wn);
   } else {
     for (int kr = threadIdx.x; kr < nr; kr += kBlock) {
       const int i = g.idx[k_lo + kr];
       s_i[kr] = (unsigned)i < (unsigned)g.F ? i : -1;
     }
+    __syncthreads();
   }
-  __syncthreads();
   const size_t rb = row_bytes<WT>(g.d);
   const char* xs = reinterpret_cast<const char*>(s_x);
+  // the layer call's list and count are stored last: nothing in the kernel waits for them
+  auto store_list = [&]() {
+    if constexpr (SCAN) {
+      for (int kr = threadIdx.x; kr < nr; kr += kBlock) {
+        const int i = s_i[kr];
+        g.idx_out[k_lo + kr] = i >= 0 ? i : 0;
+      }
+      if (s == 0 && threadIdx.x == 0) *g.count_out = n;
+    }
+  };
   if constexpr (WT == St::I4) {
     // ================= 4-bit weights
     const int ng = g.d / 128;
@@ -556,10 +585,10 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
         }
       }
     };
-    // ---- up: 16 lanes per row, 4 rows per wave, UQ 16-byte slices per lane per pass
-    constexpr int UQ = ACT == PSFFN_SWIGLU ? 12 : 24;
-    const int li = lane & 15, lg = lane >> 4;
-    const int step = UQ * 16 * 32;
+    // ---- up: 32 lanes per row, 2 rows per wave, UQ 16-byte slices per lane per pass
+    constexpr int UQ = 12;
+    const int li = lane & 31, lg = lane >> 5;
+    const int step = UQ * 32 * 32;
     const char* su_base = reinterpret_cast<const char*>(g.s_up);
     const char* sg_base = reinterpret_cast<const char*>(g.s_gate);
     uint4 wu[UQ], wg[UQ];
@@ -568,7 +597,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
     int i = -1;
     size_t ro = 0, so = 0;
     auto row_begin = [&](int k0) {
-      const int kr = k0 + wv * 4 + lg;
+      const int kr = k0 + wv * 2 + lg;
       i = kr < nr ? s_i[kr] : -1;
       ro = (size_t)(i >= 0 ? i : 0) * rb;
       so = (size_t)(i >= 0 ? i : 0) * srow;
@@ -578,7 +607,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
     auto up_load = [&](int e0) {
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
-        const int e = e0 + (q * 16 + li) * 32;
+        const int e = e0 + (q * 32 + li) * 32;
         const bool ok = i >= 0 && e < g.d;
         wu[q] = ld16z(reinterpret_cast<const char*>(g.w_up) + ro + e / 2, ok);
         su[q] = ld2z(su_base + so + (size_t)(e / 128) * 2, ok);
@@ -591,7 +620,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
     auto up_acc = [&](int e0) {
 #pragma unroll
       for (int q = 0; q < UQ; ++q) {
-        const int e = e0 + (q * 16 + li) * 32;
+        const int e = e0 + (q * 32 + li) * 32;
         const int ec = e < g.d ? e : 0;  // (the weights and scales past d are zero)
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -603,16 +632,16 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
       }
     };
     auto row_end = [&](int k0) {
-      const int kr = k0 + wv * 4 + lg;
+      const int kr = k0 + wv * 2 + lg;
       const bool valid = i >= 0;
       const float bu = (valid && g.b_up) ? g.b_up[i] : 0.f;
       const float bg = (valid && g.b_gate) ? g.b_gate[i] : 0.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float uu = sum16(uacc[b]) + bu;
+        const float uu = sum32(uacc[b]) + bu;
         float av;
         if constexpr (ACT == PSFFN_SWIGLU) {
-          av = silu_f(sum16(gacc[b]) + bg) * uu;
+          av = silu_f(sum32(gacc[b]) + bg) * uu;
         } else {
           av = uu > 0.f ? uu : 0.f;
         }
@@ -631,7 +660,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
       up_acc(e0);
     }
     row_end(0);
-    for (int k0 = 4 * (kBlock / kWave); k0 < nr; k0 += 4 * (kBlock / kWave)) {
+    for (int k0 = 2 * (kBlock / kWave); k0 < nr; k0 += 2 * (kBlock / kWave)) {
       row_begin(k0);
       for (int e0 = 0; e0 < g.d; e0 += step) {
         up_load(e0);
@@ -721,6 +750,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
         }
       }
     }
+    store_list();
     return;
   } else {
     // ================= dense weights
@@ -875,6 +905,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
         }
       }
     }
+    store_list();
   }
 }
 
@@ -886,7 +917,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
   __shared__ float4 s_sum[16][16];
   const int n = list_len(g.count, g.F);  // the layer path's up kernel wrote it
   int ks, S;
-  udsplit(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
+  udsplit<WT>(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
   const size_t total4 = (size_t)g.B * g.d / 4;
   const int q = threadIdx.x & 15, grp = threadIdx.x >> 4;
   const size_t o4 = (size_t)blockIdx.x * 16 + q;
@@ -1073,9 +1104,10 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
 template <St PT, St WT, psffn_act ACT, int NB, int RV>
 static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
-  constexpr int RPW = 8;
-  const int NQ = (P.F + 4 * RPW - 1) / (4 * RPW);
-  // the fused up/down kernel's LDS: the activations, the chunk prefix and the split's rows
+  constexpr int RPW = 4;                  // k_q chunks of 16 neurons (32 KB of Q rows in flight each)
+  const int NQ = (P.F + 31) / 32;         // 32-bit mask words
+  const int NC = (P.F + 4 * RPW - 1) / (4 * RPW);
+  // the fused up/down kernel's LDS: the activations, the mask words and the split's rows
   const size_t ud = round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2)) + round256(4 * (size_t)(2 * NQ + 1)) +
                     4 * (size_t)kUDMaxRows * NB + 4 * (size_t)kUDMaxRows;
   if (!ffn_fits<WT>(W, B) || NQ > kMaxScanChunks || (size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX ||
@@ -1088,8 +1120,8 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h, hdr);
-  k_q<PT, NB, RV, RPW, true><<<NQ, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, nullptr, nullptr, nullptr,
-                                                   nullptr, logits, NQ, masks);
+  k_q<PT, NB, RV, RPW, true><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, nullptr, nullptr, nullptr,
+                                                   nullptr, logits, NC, masks);
   FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
   g.masks = masks;
   g.nq = NQ;
