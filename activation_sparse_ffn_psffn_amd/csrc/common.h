@@ -109,36 +109,24 @@ __device__ __forceinline__ float i4_elem(uint32_t w, int k) {
 // ----------------------------------------------------------------------------------------
 // workspace layout (bytes, every region 256-byte aligned)
 //
-//   [0, 256)      header words: call epoch, error bits
-//   chunk states  one 64-bit word per predictor chunk of >= 16 neurons, and one per group of 64
-//                 chunks (the two-level scan of the compaction), tagged with the call epoch so
-//                 that no reset is ever needed
-//   mask words    one 32-bit word of active bits per 32 neurons (one-call layer path)
-//   tile words    per-column-tile "partials done" counters of the down projection, left zero
-//                 by the last workgroup of each tile
+//   [0, 256)      reserved header
+//   mask words    one 32-bit word of active bits per 32 neurons (predictor -> list / fused FFN)
 //   scratch       per-call buffers (h, flags, activations, partials); dead between calls
 // The layout depends on F only, so the predictor and the FFN of one layer can share one
-// workspace.  A fresh workspace must be zero-filled once (psffn_workspace_init).
+// workspace.  No region carries state from one call to the next.
 
-constexpr int kMaxTiles = 1024;  // max column tiles of the down projection (d <= kMaxD)
 constexpr int kMaxD = 262144;
-constexpr int kMinChunk = 16;  // smallest predictor chunk (neurons)
-enum HeaderWord : int { kEpoch = 0, kErr = 3 };
 
 __host__ __device__ inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct StateLayout {
-  size_t chunk_state, group_state, masks, tile_done, scratch;
+  size_t masks, scratch;
 };
 
 __host__ __device__ inline StateLayout state_layout(int F) {
   StateLayout s;
-  const size_t chunks = (size_t)(F + kMinChunk - 1) / kMinChunk;
-  s.chunk_state = 256;
-  s.group_state = s.chunk_state + round256(8 * chunks);
-  s.masks = s.group_state + round256(8 * ((chunks + 63) / 64));
-  s.tile_done = s.masks + round256(4 * (size_t)((F + 31) / 32));
-  s.scratch = s.tile_done + round256(4 * (size_t)kMaxTiles);
+  s.masks = 256;
+  s.scratch = s.masks + round256(4 * (size_t)((F + 31) / 32));
   return s;
 }
 

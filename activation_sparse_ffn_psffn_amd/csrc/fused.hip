@@ -1,82 +1,48 @@
-// Small-batch pipeline (B <= 4), four kernels per layer:
+// Small-batch pipeline (B <= 4).  Layer call, four kernels:
 //
 //   k_h     h = A x                       one wave per row of A, all of a row's loads in flight
-//   k_q     l = Q h + c, threshold; the ascending active list by decoupled look-back (predict
-//           call) or one mask word per 32 neurons (layer call)
-//   k_ud    per split of the list: a_k = act(W_up[idx[k]] . x (+ gate branch)), then the split's
-//           partial of sum_k a_k W_dT[idx[k]] (the layer call orders the list from the mask words)
+//   k_q     l = Q h + c, threshold; one bit per neuron (mask words, 16 neurons per workgroup)
+//   k_ud    per split of the active list (ordered from the mask words in each workgroup):
+//           a_k = act(W_up[idx[k]] . x (+ gate branch)), then the split's partial of
+//           sum_k a_k W_dT[idx[k]]
 //   k_reduce_ud  y = b_down + the split partials summed in split order (+ y when accumulating)
+//
+// The predictor call runs k_h, k_q and k_list (one workgroup: mask words -> ascending list);
+// the FFN call runs k_ud from a given list, then k_reduce_ud.
 //
 // Method ("PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU", Elamur
 // Research summary): Summary 2nd paragraph (a per-layer predictor guesses the firing neurons;
 // neuron-level kernels compute those and skip the rest) and Interesting ideas I4 (work directly
 // on whole weight rows and columns).
 //
-// Why kernel boundaries and not in-kernel waits: measured on MI355X, a dependency resolved inside
-// a kernel costs a coherent memory round trip while every HBM queue is full (several µs), and a
-// shared counter that ~1000 workgroups touch serialises at ~7 ns per access.  The only in-kernel
-// wait left is the look-back of k_q, where chunks finish staggered in dispatch order and a chunk
-// usually finds its predecessor's prefix already published.  The up -> down dependency stays
-// inside one workgroup of k_ud (its rows' activations never leave LDS).
+// Why kernel boundaries and not in-kernel waits: measured on MI355X, back-to-back launches cost
+// ~1-2 µs each, while a grid-wide barrier inside a persistent launch (one workgroup per CU, a
+// device-scope counter polled with s_sleep) cost ~9 µs, more when the next phase's loads were
+// already in flight.  So every cross-workgroup dependency is a kernel boundary; the up -> down
+// dependency stays inside one workgroup of k_ud (its rows' activations never leave LDS).
 //
-// Cross-workgroup words (look-back states) are read and written
-// with relaxed device-scope atomics: on gfx950 those carry the sc1 bit, each access is coherent
-// across the XCDs' separate L2 caches on its own, and polling them costs no cache maintenance.
-// A writer waits for its data stores to complete (s_waitcnt) before bumping a counter; a reader
-// loads data only after it has observed the counter.
+// Loads are unconditional wherever the compiler would otherwise branch around them: a lane with
+// nothing to load reads a 16-byte zero block instead.  A load behind a branch makes the compiler
+// wait for every outstanding load at the join, which serialises independent row streams.
 #include "common.h"
 
 namespace psffn {
 
-constexpr uint32_t kSpinLimit = 1u << 22;
-
-__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned long long ld_relaxed(const unsigned long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_relaxed(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_relaxed(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t add_relaxed(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// wait until this wave's outstanding memory operations (the published data) have completed
-__device__ __forceinline__ void stores_done() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Value of a state word (epoch << 32 | value) once it carries this call's epoch.  Bounded: on
-// timeout the error bit is set and 0 is returned.
-__device__ __forceinline__ uint32_t wait_epoch(const unsigned long long* p, unsigned long long epoch, uint32_t* err) {
-  unsigned long long w = ld_relaxed(p);
-  uint32_t it = 0;
-  while ((w >> 32) != epoch && it++ < kSpinLimit) {
-    __builtin_amdgcn_s_sleep(1);
-    w = ld_relaxed(p);
-  }
-  if ((w >> 32) != epoch) {
-    atomicOr(err, 2u);
-    return 0u;
-  }
-  return (uint32_t)w;
-}
-
-__device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// read through this block when a lane has nothing to load (keeps every load unconditional)
+__device__ uint4 g_zero_ud[1] = {{0u, 0u, 0u, 0u}};  // never written
+
+__device__ __forceinline__ uint4 ld16z(const void* p, bool ok) {
+  return *reinterpret_cast<const uint4*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+__device__ __forceinline__ uint2 ld8z(const void* p, bool ok) {
+  return *reinterpret_cast<const uint2*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+__device__ __forceinline__ uint32_t ld2z(const void* p, bool ok) {
+  return (uint32_t)*reinterpret_cast<const uint16_t*>(ok ? p : static_cast<const void*>(g_zero_ud));
+}
+
 
 constexpr int kStageX = 65536;  // bytes of LDS for the activations of all tokens (B * d * elem)
 
@@ -97,16 +63,14 @@ __device__ __forceinline__ void stage_x(const void* __restrict__ x, size_t n, ui
 
 // =========================================================================================
 // k_h: h[b][j] = A[j] . x_b.  One wave per row, up to 16 slices of 16 B in flight per lane.
-// Block 0 also advances the call epoch that tags this call's look-back states.
 
 template <St PT, int NB>
 __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const void* __restrict__ x, int d, int r,
-                                              int nb, float* __restrict__ h, uint32_t* __restrict__ hdr) {
+                                              int nb, float* __restrict__ h) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int UN = 16;
   extern __shared__ uint4 s_x[];  // B * d activations (dynamic size)
-  if (blockIdx.x == 0 && threadIdx.x == 0) hdr[kEpoch] = hdr[kEpoch] + 1u;
   const int lane = wave_lane();
   const int j = blockIdx.x * (kBlock / kWave) + wave_id();
   const char* arow = reinterpret_cast<const char*>(A) + (size_t)(j < r ? j : 0) * d * ESZ;
@@ -116,7 +80,7 @@ __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const 
 #pragma unroll
   for (int u = 0; u < UN; ++u) {
     const int e = base + u * kWave * EPL;
-    w[u] = (j < r && e < d) ? ld16(arow + (size_t)e * ESZ) : make_uint4(0, 0, 0, 0);
+    w[u] = ld16z(arow + (size_t)e * ESZ, j < r && e < d);
   }
   stage_x(x, (size_t)nb * d * ESZ, s_x);
   if (j >= r) return;
@@ -139,7 +103,7 @@ __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const 
 #pragma unroll
     for (int u = 0; u < UN; ++u) {
       const int e = base + u * kWave * EPL;
-      w[u] = e < d ? ld16(arow + (size_t)e * ESZ) : make_uint4(0, 0, 0, 0);
+      w[u] = ld16z(arow + (size_t)e * ESZ, e < d);
     }
   }
 #pragma unroll
@@ -152,20 +116,16 @@ __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const 
 // =========================================================================================
 // k_q: chunk q = blockIdx.x covers neurons [q*4*RPW, (q+1)*4*RPW), RPW per wave.  All Q row
 // loads are issued first; h (fp32, from the previous kernel) is read next; then logits, the
-// union test over the batch, and the chunk's place in the ascending list.
+// union test over the batch, and the chunk's mask bits.
 
-template <St PT, int NB, int RV, int RPW, bool MASKS>
+template <St PT, int NB, int RV, int RPW>
 __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const float* __restrict__ c,
                                               const float* __restrict__ h, int r, int F, float thr, int nb,
-                                              uint32_t* __restrict__ hdr, unsigned long long* __restrict__ cstate,
-                                              unsigned long long* __restrict__ gstate, int32_t* __restrict__ idx,
-                                              int32_t* __restrict__ count, float* __restrict__ logits, int NQ,
-                                              uint32_t* __restrict__ masks) {
+                                              float* __restrict__ logits, int NQ, uint32_t* __restrict__ masks) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int ROWS = 4 * RPW;
   __shared__ uint32_t s_mask[kBlock / kWave];
-  __shared__ int s_base;
   const int lane = wave_lane(), wv = wave_id();
   const int q = blockIdx.x;
   const int i0 = q * ROWS + wv * RPW;
@@ -175,10 +135,8 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
 #pragma unroll
     for (int v = 0; v < RV; ++v) {
       const int i = i0 + k, e = v * kWave * EPL + lane * EPL;
-      qv[k][v] = (i < F && e < r) ? ld16(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ)
-                                  : make_uint4(0, 0, 0, 0);
+      qv[k][v] = ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && e < r);
     }
-  const unsigned long long epoch = hdr[kEpoch];
   float hv[NB][RV][EPL];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -228,63 +186,67 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
   }
   if (lane == 0) s_mask[wv] = mask;
   __syncthreads();
-  if constexpr (MASKS) {
-    // layer path: publish the chunk's active bits only; the up kernel orders them.  Chunks of 16
-    // neurons write the halves of the 32-bit words (little endian); an odd last chunk writes its
-    // whole word, so the unused upper half reads as zero.
-    static_assert(4 * RPW == 32 || 4 * RPW == 16, "chunks of 32 or 16 neurons");
-    if (threadIdx.x == 0) {
-      const uint32_t bits = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
-      if constexpr (4 * RPW == 32) {
-        masks[q] = bits;
-      } else if ((q & 1) == 0 && q == NQ - 1) {
-        masks[q >> 1] = bits;
-      } else {
-        reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
-      }
+  // the chunk's active bits.  Chunks of 16 neurons write the halves of the 32-bit words (little
+  // endian); an odd last chunk writes its whole word, so the unused upper half reads as zero.
+  static_assert(4 * RPW == 32 || 4 * RPW == 16, "chunks of 32 or 16 neurons");
+  if (threadIdx.x == 0) {
+    const uint32_t bits = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
+    if constexpr (4 * RPW == 32) {
+      masks[q] = bits;
+    } else if ((q & 1) == 0 && q == NQ - 1) {
+      masks[q >> 1] = bits;
+    } else {
+      reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
     }
-    return;
   }
-  int cnt = 0;
-#pragma unroll
-  for (int w = 0; w < kBlock / kWave; ++w) cnt += __popc(s_mask[w]);
-  // ---- place in the ascending list: a two-level scan.  Chunk q publishes its count; wave 0
-  // reads the counts of the earlier chunks of its group of 64 (one load per lane); the last
-  // chunk of a group publishes the group total; the chunk then reads the totals of the earlier
-  // groups (one load per lane per 64 groups).  No dependency chain is longer than one group, so
-  // chunks that all finish together do not walk back one window at a time.  Words are tagged
-  // with the call epoch: a word from an earlier call counts as not yet published.
-  if (wv == 0) {
-    const unsigned long long tag = epoch << 32;
-    if (lane == 0) st_relaxed(&cstate[q], tag | (uint32_t)cnt);
-    const int g = q / kWave;
-    int pre = 0;
-    {
-      const int jj = g * kWave + lane;
-      uint32_t v = 0;
-      if (jj < q) v = wait_epoch(&cstate[jj], epoch, &hdr[kErr]);
-      pre = wave_sum_int((int)v);
-    }
-    if (q % kWave == kWave - 1 || q == NQ - 1) {
-      if (lane == 0) st_relaxed(&gstate[g], tag | (uint32_t)(pre + cnt));
-    }
-    for (int g0 = 0; g0 < g; g0 += kWave) {
-      const int gg = g0 + lane;
-      uint32_t v = 0;
-      if (gg < g) v = wait_epoch(&gstate[gg], epoch, &hdr[kErr]);
-      pre += wave_sum_int((int)v);
-    }
-    if (lane == 0) s_base = pre;
-  }
+}
+
+// =========================================================================================
+// k_list: one workgroup turns the mask words into the ascending list of active neurons and its
+// length (the standalone predictor call; the layer call orders the list inside k_ud).  Thread t
+// owns the consecutive words [t per, t per + per): a block scan of their popcounts gives its first
+// list position, then it writes the ids of its words in order.
+
+constexpr int kListThreads = 1024;
+
+__global__ __launch_bounds__(kListThreads) void k_list(const uint32_t* __restrict__ masks, int nq, int F,
+                                                       int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+  extern __shared__ uint32_t s_m[];  // nq mask words
+  __shared__ int s_red[kListThreads / kWave];
+  for (int q = threadIdx.x; q < nq; q += kListThreads) s_m[q] = masks[q];
   __syncthreads();
-  int wpre = 0;
-  for (int w = 0; w < wv; ++w) wpre += __popc(s_mask[w]);
-  const uint32_t m = s_mask[wv];
-  if (lane < RPW && ((m >> lane) & 1u)) {
-    const int at = s_base + wpre + __popc(m & ((1u << lane) - 1u));
-    if (at < F) idx[at] = i0 + lane;
+  const int per = (nq + kListThreads - 1) / kListThreads;
+  const int q0 = threadIdx.x * per;
+  int tot = 0;
+  for (int u = 0; u < per; ++u)
+    if (q0 + u < nq) tot += __popc(s_m[q0 + u]);
+  const int lane = wave_lane(), wv = wave_id();
+  int inc = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += t;
   }
-  if (q == NQ - 1 && threadIdx.x == 0) *count = min(s_base + cnt, F);
+  if (lane == kWave - 1) s_red[wv] = inc;
+  __syncthreads();
+  int at = inc - tot, n = 0;
+#pragma unroll
+  for (int w = 0; w < kListThreads / kWave; ++w) {
+    if (w < wv) at += s_red[w];
+    n += s_red[w];
+  }
+  if (threadIdx.x == 0) *count = n < F ? n : F;
+  for (int u = 0; u < per; ++u) {
+    const int q = q0 + u;
+    if (q >= nq) break;
+    uint32_t m = s_m[q];
+    while (m != 0u) {
+      const int i = q * 32 + (int)__builtin_ctz(m);
+      m &= m - 1u;
+      if (at < F) idx[at] = i;
+      ++at;
+    }
+  }
 }
 
 // =========================================================================================
@@ -313,7 +275,6 @@ struct FfnArgs {
   const int32_t* count;
   float* a;
   float* part;
-  uint32_t* hdr;
   float* y;
   int B, d, F, accumulate;
 };
@@ -429,19 +390,6 @@ template <St WT>
 __host__ __device__ inline int ud_stream_bytes(int d, psffn_act act) {
   const int rb = WT == St::F32 ? 4 * d : (WT == St::F16 ? 2 * d : d / 2 + 2 * (d / 128));
   return (act == PSFFN_SWIGLU ? 3 : 2) * rb;
-}
-
-// read through this block when a lane has nothing to load (keeps every load unconditional)
-__device__ uint4 g_zero_ud[1] = {{0u, 0u, 0u, 0u}};  // never written
-
-__device__ __forceinline__ uint4 ld16z(const void* p, bool ok) {
-  return *reinterpret_cast<const uint4*>(ok ? p : static_cast<const void*>(g_zero_ud));
-}
-__device__ __forceinline__ uint2 ld8z(const void* p, bool ok) {
-  return *reinterpret_cast<const uint2*>(ok ? p : static_cast<const void*>(g_zero_ud));
-}
-__device__ __forceinline__ uint32_t ld2z(const void* p, bool ok) {
-  return (uint32_t)*reinterpret_cast<const uint16_t*>(ok ? p : static_cast<const void*>(g_zero_ud));
 }
 
 // 4-bit decode with the sign bits pre-flipped (w ^ 0x88888888): the pair of nibbles at bits
@@ -963,19 +911,18 @@ __global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
 template <St PT, int NB, int RV>
 static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx, int32_t* count,
                             float* logits, void* ws, hipStream_t s) {
-  constexpr int RPW = 8;
+  constexpr int RPW = 4;               // k_q chunks of 16 neurons
+  const int NC = (P.F + 4 * RPW - 1) / (4 * RPW);
+  const int NQ = (P.F + 31) / 32;      // 32-bit mask words
+  if ((size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX || NQ > kMaxScanChunks) return hipErrorNotSupported;
   const StateLayout L = state_layout(P.F);
   char* w = static_cast<char*>(ws);
-  uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
-  unsigned long long* cstate = reinterpret_cast<unsigned long long*>(w + L.chunk_state);
-  unsigned long long* gstate = reinterpret_cast<unsigned long long*>(w + L.group_state);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
-  const int NQ = (P.F + 4 * RPW - 1) / (4 * RPW);
-  if ((size_t)B * P.d * Tr<PT>::ESZ > (size_t)kStageX) return hipErrorNotSupported;
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h, hdr);
-  k_q<PT, NB, RV, RPW, false><<<NQ, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, cstate, gstate, idx, count,
-                                                    logits, NQ, nullptr);
+  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
+  k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
   return hipGetLastError();
 }
 
@@ -1033,7 +980,6 @@ static FfnArgs ffn_args(const psffn_ffn& W, const void* x, int B, const int32_t*
   g.count = count;
   g.a = reinterpret_cast<float*>(w + L.scratch);
   g.part = reinterpret_cast<float*>(w + L.scratch + round256((size_t)W.F * B * 4));
-  g.hdr = reinterpret_cast<uint32_t*>(w);
   g.y = y;
   g.B = B;
   g.d = W.d;
@@ -1115,13 +1061,11 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
     return hipErrorNotSupported;
   const StateLayout L = state_layout(P.F);
   char* w = static_cast<char*>(ws);
-  uint32_t* hdr = reinterpret_cast<uint32_t*>(w);
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h, hdr);
-  k_q<PT, NB, RV, RPW, true><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, hdr, nullptr, nullptr, nullptr,
-                                                   nullptr, logits, NC, masks);
+  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
   FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
   g.masks = masks;
   g.nq = NQ;
