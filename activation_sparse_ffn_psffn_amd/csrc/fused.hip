@@ -47,32 +47,36 @@ __device__ __forceinline__ uint32_t ld2z(const void* p, bool ok) {
 constexpr int kStageX = 65536;  // bytes of LDS for the activations of all tokens (B * d * elem)
 
 // Copy n bytes of activations into LDS (16-byte pieces, all in flight at once), then barrier.
+// NT = threads of the workgroup.
+template <int NT>
 __device__ __forceinline__ void stage_x(const void* __restrict__ x, size_t n, uint4* s_x) {
   const uint4* src = reinterpret_cast<const uint4*>(x);
   const int n16 = (int)(n / 16);
-  for (int k0 = threadIdx.x; k0 < n16; k0 += 8 * kBlock) {
+  for (int k0 = threadIdx.x; k0 < n16; k0 += 8 * NT) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = k0 + u * kBlock < n16 ? src[k0 + u * kBlock] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 8; ++u) v[u] = k0 + u * NT < n16 ? src[k0 + u * NT] : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (k0 + u * kBlock < n16) s_x[k0 + u * kBlock] = v[u];
+      if (k0 + u * NT < n16) s_x[k0 + u * NT] = v[u];
   }
   __syncthreads();
 }
 
 // =========================================================================================
 // k_h: h[b][j] = A[j] . x_b.  One wave per row, up to 16 slices of 16 B in flight per lane.
+// (Two-wave workgroups, twice as many, measured 0.4 µs slower on a 1024 x 7168 fp16 A.)
+constexpr int kHThreads = 256;
 
 template <St PT, int NB>
-__global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const void* __restrict__ x, int d, int r,
+__global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, const void* __restrict__ x, int d, int r,
                                               int nb, float* __restrict__ h) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int UN = 16;
   extern __shared__ uint4 s_x[];  // B * d activations (dynamic size)
   const int lane = wave_lane();
-  const int j = blockIdx.x * (kBlock / kWave) + wave_id();
+  const int j = blockIdx.x * (kHThreads / kWave) + wave_id();
   const char* arow = reinterpret_cast<const char*>(A) + (size_t)(j < r ? j : 0) * d * ESZ;
   // this wave's row loads go out first, then the workgroup stages x (all tokens) in LDS
   uint4 w[UN];
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kBlock) void k_h(const void* __restrict__ A, const 
     const int e = base + u * kWave * EPL;
     w[u] = ld16z(arow + (size_t)e * ESZ, j < r && e < d);
   }
-  stage_x(x, (size_t)nb * d * ESZ, s_x);
+  stage_x<kHThreads>(x, (size_t)nb * d * ESZ, s_x);
   if (j >= r) return;
   const char* xs = reinterpret_cast<const char*>(s_x);
   float acc[NB];
@@ -858,18 +862,21 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
 }
 
 // y = (accumulate ? y : 0) + (b_down + the S split partials summed in split order).  Workgroup =
-// 64 consecutive outputs (16 float4); its 16 thread groups take consecutive ranges of splits, and
-// the group sums are added in group order.
+// kRQ float4 columns (4 kRQ consecutive outputs); its kRG thread groups take consecutive ranges
+// of splits (at most 8 loads each in flight), and the group sums are added in group order.
+constexpr int kRQ = 8;
+constexpr int kRG = kBlock / kRQ;
+
 template <St WT, psffn_act ACT>
 __global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
-  __shared__ float4 s_sum[16][16];
+  __shared__ float4 s_sum[kRG][kRQ];
   const int n = list_len(g.count, g.F);  // the layer path's up kernel wrote it
   int ks, S;
   udsplit<WT>(n, g.B, g.d, ud_stream_bytes<WT>(g.d, ACT), ks, S);
   const size_t total4 = (size_t)g.B * g.d / 4;
-  const int q = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  const size_t o4 = (size_t)blockIdx.x * 16 + q;
-  const int per = (S + 15) / 16;
+  const int q = threadIdx.x % kRQ, grp = threadIdx.x / kRQ;
+  const size_t o4 = (size_t)blockIdx.x * kRQ + q;
+  const int per = (S + kRG - 1) / kRG;
   const int s0 = grp * per, s1 = min(S, s0 + per);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (o4 < total4) {
@@ -895,7 +902,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) t[c] = g.b_down[col + c];
     }
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kRG; ++k) {
       const float4 v = s_sum[k][q];
       t[0] += v.x; t[1] += v.y; t[2] += v.z; t[3] += v.w;
     }
@@ -920,7 +927,7 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
   k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
   return hipGetLastError();
@@ -1012,7 +1019,7 @@ static hipError_t ffn_launch(const FfnArgs& g, hipStream_t s) {
   int grid = kUDSplitCap;
   if (grid > g.F) grid = g.F;
   k_ud<WT, ACT, NB, SCAN><<<grid, kBlock, lds, s>>>(g);
-  k_reduce_ud<WT, ACT><<<(unsigned)(((size_t)g.B * g.d / 4 + 15) / 16), kBlock, 0, s>>>(g);
+  k_reduce_ud<WT, ACT><<<(unsigned)(((size_t)g.B * g.d / 4 + kRQ - 1) / kRQ), kBlock, 0, s>>>(g);
   return hipGetLastError();
 }
 
@@ -1064,7 +1071,7 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + 3) / 4, kBlock, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
   FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
   g.masks = masks;
