@@ -36,8 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 # (hash below); after any change to them the traffic is reported as null until measured again.
 TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/fused.hip")
 TRAFFIC = {
-    # (workload, batch): fetch KiB k_h 7262.6 + k_q 28898.8, write KiB 8.0 + 34.6
-    ("opt30b_relu_f16", 1): {"sources": "b839f9a22c632184", "bytes": 74102170},
+    # (workload, batch): fetch KiB k_h 7261.1 + k_q 28822.8 + k_list 4.1, write KiB 8.0 + 28.0 + 3.4
+    ("opt30b_relu_f16", 1): {"sources": "7e1fd5023c8875b3", "bytes": 73948570},
 }
 
 
@@ -245,8 +245,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(spec.name, B),
-                "kernel": "psffn_predict (k_h + k_q at B <= 4; the batch predictor kernels above): the fp16 "
-                          "predictor stream A then Q, threshold, ordered list",
+                "kernel": "psffn_predict (k_h, k_q, k_list at B <= 4; the batch predictor kernels above): the "
+                          "fp16 predictor stream A then Q, threshold, mask words, ordered list",
                 "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
         del g_pred, g_ffn, idx_all
 
