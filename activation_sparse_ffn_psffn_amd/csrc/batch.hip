@@ -198,40 +198,62 @@ __device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t
 // =============================================================================================
 // k_bh: wave (row tile rt, chunk kc): partial h over d-elements [512 kc, 512 kc + 512) of rows
 // [16 rt, 16 rt + 16).  Grid (ceil(d / 512), ceil(r / 64)): consecutive workgroups read consecutive
-// chunks of the same 64 rows; the 4 waves of a workgroup share the chunk of x through L1.  Every load of the wave (A rows, x fragments) is issued before the first
-// MFMA: one memory round trip per wave.  hpart[kc][n][j], n < NBP (padded tokens give zeros).
+// chunks of the same 64 rows.  Each wave requests its 16 A fragments first (buffer loads: rows
+// past r and columns past d read zeros), then the workgroup stages the chunk of x (all padded
+// token rows) in LDS once; the MFMAs read their x fragments from there.  One memory round trip
+// per wave.  hpart[kc][n][j], n < NBP (padded tokens give zeros).
 
 template <int NT>
 __global__ __launch_bounds__(kBlock) void k_bh(BArgs g) {
+  constexpr int NBP = 16 * NT;
+  constexpr int XP = kHChunk + 8;  // LDS pitch (elements): rows 16 bytes apart in bank order
+  __shared__ __align__(16) uint16_t s_xc[NBP * XP];
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4;
   const int rt = blockIdx.y * 4 + wave_id();
   const int kc = blockIdx.x;
-  if (rt * 16 >= g.r) return;
-  const int row = rt * 16 + li;
   const int d = g.d;
-  const uint16_t* arow = g.A + (size_t)(row < g.r ? row : 0) * d;
-  uint4 xv[NT][16], w[16];
+  const __amdgpu_buffer_rsrc_t ar = rsrc(g.A, (uint32_t)((size_t)g.r * d * 2));
+  const __amdgpu_buffer_rsrc_t xr = rsrc(g.x, (uint32_t)((size_t)g.B * d * 2));
+  const int row = rt * 16 + li;
+  const uint32_t rbase = row < g.r ? (uint32_t)((size_t)row * d * 2) : kNoRow;
+  uint4 w[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int e = kc * kHChunk + (j >> 2) * 128 + lg * 32 + (j & 3) * 8;
+    w[j] = bld16(ar, e < d ? rbase + (uint32_t)e * 2 : kNoRow);
+  }
+  {
+    constexpr int PIECES = NBP * (kHChunk / 8);  // 16-byte pieces of the x chunk
+    constexpr int PPT = PIECES / kBlock;
+    static_assert(PIECES % kBlock == 0, "whole pieces per thread");
+    uint4 xv[PPT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int n = t * 16 + li;
-      xv[t][j] = (n < g.B && e < d) ? ldg16(g.x + (size_t)n * d + e) : zero4();
+    for (int k = 0; k < PPT; ++k) {
+      const int pc = threadIdx.x + k * kBlock;
+      const int n = pc / (kHChunk / 8), e = kc * kHChunk + (pc % (kHChunk / 8)) * 8;
+      xv[k] = bld16(xr, (n < g.B && e < d) ? (uint32_t)((size_t)n * d + e) * 2 : kNoRow);
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int pc = threadIdx.x + k * kBlock;
+      const int n = pc / (kHChunk / 8), e8 = pc % (kHChunk / 8);
+      *reinterpret_cast<uint4*>(&s_xc[n * XP + e8 * 8]) = xv[k];
     }
   }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int e = kc * kHChunk + (j >> 2) * 128 + lg * 32 + (j & 3) * 8;
-    w[j] = (row < g.r && e < d) ? ldg16(arow + e) : zero4();
-  }
+  __syncthreads();
+  if (rt * 16 >= g.r) return;
   f4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int j = 0; j < 16; ++j) {
+    const int el = (j >> 2) * 128 + lg * 32 + (j & 3) * 8;  // element within the chunk
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = mma(as_h8(w[j]), as_h8(xv[t][j]), acc[t]);
+    for (int t = 0; t < NT; ++t) {
+      const uint4 xf = *reinterpret_cast<const uint4*>(&s_xc[(t * 16 + li) * XP + el]);
+      acc[t] = mma(as_h8(w[j]), as_h8(xf), acc[t]);
+    }
+  }
   const int j0 = rt * 16 + 4 * lg;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -501,7 +523,7 @@ __global__ __launch_bounds__(kBqThreads) void k_bq_lds(BArgs g) {
 
 __host__ __device__ inline int bq_full_pitch(int nkb) { return nkb * 256 + 16; }
 
-constexpr int kBqFullThreads = 512;  // one workgroup per CU, two waves per SIMD
+constexpr int kBqFullThreads = 256;  // one workgroup per CU (h in LDS), four waves: at most 4 row tiles (<= 192 KB) in flight per CU
 
 template <int NT, int NKB>
 __global__ __launch_bounds__(kBqFullThreads) void k_bq_full(BArgs g) {
@@ -1115,7 +1137,8 @@ size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_ac
 }
 
 bool batch_supported_pred(const psffn_predictor& P, int B) {
-  return B > kFusedMaxBatch && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF;
+  return B > kFusedMaxBatch && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF &&
+         (size_t)P.r * P.d * 2 <= kMaxBufferBytes;  // k_bh reads A through one buffer resource
 }
 bool batch_supported_ffn(const psffn_ffn& W, int B) {
   const size_t rowb = W.dt == PSFFN_I4G128 ? (size_t)W.d / 2 : (size_t)W.d * 2;
