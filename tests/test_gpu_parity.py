@@ -23,6 +23,11 @@ CASES = [
     ("i4_relu", "opt175b_relu_i4", dict(d=1152, F=1200, r=64, density=0.08)),
     ("i4_swiglu", "opt175b_relu_i4", dict(d=640, F=700, r=32, act="swiglu", density=0.4)),
     ("f32_swiglu", "tiny_relu_f32", dict(d=136, F=333, r=16, act="swiglu", density=0.3)),
+    # rows wider than one pass of the small-batch kernels (fp16 > 8192, fp32 > 4096, 4-bit > 12288
+    # elements) and more column slices than one pass of the down projection
+    ("f16_relu_wide", "opt30b_relu_f16", dict(d=8200, F=600, r=24, density=0.1)),
+    ("f32_relu_wide", "tiny_relu_f32", dict(d=4104, F=300, r=16)),
+    ("i4_relu_wide", "opt175b_relu_i4", dict(d=12416, F=400, r=24, density=0.1)),
 ]
 
 _cache = {}
