@@ -778,23 +778,65 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
       }
     };
     // the first row's first pass goes out before the first down batch, which then streams while
-    // the up rows are reduced
-    row_begin(wv);
-    up_load(0);
-    load_down(0, 0);
-    up_acc(0);
-    for (int e0 = step; e0 < g.d; e0 += step) {
-      up_load(e0);
-      up_acc(e0);
-    }
-    row_end(wv);
-    for (int k0 = kBlock / kWave; k0 < nr; k0 += kBlock / kWave) {
-      row_begin(k0 + wv);
-      for (int e0 = 0; e0 < g.d; e0 += step) {
+    // the up rows are reduced.  With several tokens (more arithmetic per row) and rows of one pass,
+    // a wave requests its next row before it reduces the current one (a second register set).
+    constexpr bool kDoubleRow = NB > 1;
+    if (kDoubleRow && g.d <= step) {
+      constexpr int NW = kBlock / kWave;
+      uint4 nu_[kDoubleRow ? UN : 1], ng_[kDoubleRow ? UN : 1];
+      int ni = -1;
+      size_t nro = 0;
+      auto next_load = [&](int kr) {
+        ni = kr < nr ? s_i[kr] : -1;
+        nro = (size_t)(ni >= 0 ? ni : 0) * rb;
+#pragma unroll
+        for (int q = 0; q < (kDoubleRow ? UN : 1); ++q) {
+          const int e = (q * kWave + lane) * EPL;
+          const bool ok = ni >= 0 && e < g.d;
+          const size_t off = nro + (size_t)e * Tr<WT>::ESZ;
+          nu_[q] = ld16z(reinterpret_cast<const char*>(g.w_up) + off, ok);
+          if constexpr (ACT == PSFFN_SWIGLU) ng_[q] = ld16z(reinterpret_cast<const char*>(g.w_gate) + off, ok);
+        }
+      };
+      auto take_next = [&]() {
+        i = ni;
+        ro = nro;
+#pragma unroll
+        for (int q = 0; q < (kDoubleRow ? UN : 1); ++q) {
+          wu[q] = nu_[q];
+          if constexpr (ACT == PSFFN_SWIGLU) wg[q] = ng_[q];
+        }
+      };
+      row_begin(wv);
+      up_load(0);
+      load_down(0, 0);
+      for (int k0 = 0; k0 < nr; k0 += NW) {
+        next_load(k0 + NW + wv);  // (past the split: the zero block)
+        up_acc(0);
+        row_end(k0 + wv);
+        if (k0 + NW >= nr) break;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) uacc[b] = gacc[b] = 0.f;
+        take_next();
+      }
+    } else {
+      row_begin(wv);
+      up_load(0);
+      load_down(0, 0);
+      up_acc(0);
+      for (int e0 = step; e0 < g.d; e0 += step) {
         up_load(e0);
         up_acc(e0);
       }
-      row_end(k0 + wv);
+      row_end(wv);
+      for (int k0 = kBlock / kWave; k0 < nr; k0 += kBlock / kWave) {
+        row_begin(k0 + wv);
+        for (int e0 = 0; e0 < g.d; e0 += step) {
+          up_load(e0);
+          up_acc(e0);
+        }
+        row_end(k0 + wv);
+      }
     }
     __syncthreads();
     // ---- down: thread t owns 16-byte column slices t + u kBlock; the next batch of RB rows is
