@@ -523,10 +523,15 @@ __global__ __launch_bounds__(kBqThreads) void k_bq_lds(BArgs g) {
 
 __host__ __device__ inline int bq_full_pitch(int nkb) { return nkb * 256 + 16; }
 
-constexpr int kBqFullThreads = 256;  // one workgroup per CU (h in LDS), four waves: at most 4 row tiles (<= 192 KB) in flight per CU
+// one workgroup per CU (h in LDS).  16 tokens: four waves (at most 4 row tiles, <= 192 KB, in
+// flight per CU: measured 32.5 us against 38.5 with eight on a 49152 x 1536 Q); 32 tokens: eight
+// waves (twice the MFMA work per tile: 20.0 us against 21.6 with four on 32768 x 1024)
+template <int NT>
+__host__ __device__ constexpr int bq_full_threads() { return NT == 1 ? 256 : 512; }
 
 template <int NT, int NKB>
-__global__ __launch_bounds__(kBqFullThreads) void k_bq_full(BArgs g) {
+__global__ __launch_bounds__(bq_full_threads<NT>()) void k_bq_full(BArgs g) {
+  constexpr int kBqFullThreads = bq_full_threads<NT>();
   constexpr int NBP = 16 * NT;
   constexpr int HP = NKB * 256 + 16;
   constexpr int WPG = kBqFullThreads / kWave;
@@ -1245,6 +1250,7 @@ static hipError_t pred_launch(const BArgs& g, hipStream_t s) {
   const int nkb_t = nkb <= 4 ? 4 : (nkb <= 8 ? 8 : 12);
   const size_t lds_full = 2 * (size_t)nbp * bq_full_pitch(nkb_t);
   if (nkb <= 12 && lds_full <= (size_t)160 * 1024 && (size_t)g.F * g.r * 2 <= kMaxBufferBytes) {
+    constexpr int kBqFullThreads = bq_full_threads<NT>();
     const int tiles = (g.F + 15) / 16, per_wg = kBqFullThreads / kWave;
     int grid = cu_count();
     if (grid > (tiles + per_wg - 1) / per_wg) grid = (tiles + per_wg - 1) / per_wg;
