@@ -883,6 +883,12 @@ __host__ __device__ constexpr size_t bdown_lds() {
   return (size_t)16 * NT * bdown_apitch<WT, NT>() + (size_t)bdown_chunk_rows<WT, NT>() * 4;
 }
 
+typedef short s4_t __attribute__((ext_vector_type(4)));
+// gfx950 transposing LDS read of four 16-bit elements (one 8-byte piece named per lane)
+__device__ __forceinline__ s4_t lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)(p));
+}
+
 // 8 nibbles (columns c..c+7 of one row) -> 8 fp16 in column order: each byte pair of the
 // flipped nibbles is placed under the fp16 exponent of 1024 (1024 + q + 8 exactly), then 1032 is
 // subtracted from both halves
@@ -1049,10 +1055,13 @@ __global__ __launch_bounds__(kBlock) void k_bdown(BArgs g) {
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        h8_t fa;
-        const char* src = wbuf + (lg * 8) * kDPitch + (m * 16 + li) * 2;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fa[j] = *reinterpret_cast<const _Float16*>(src + j * kDPitch);
+        // A operand (column 16 m + li, rows 8 lg .. 8 lg + 8) by two transposing LDS reads: within
+        // a group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces named by lanes
+        // i / 4 + 4 j (j < 4), so lane 4 j + a names row 8 lg + 4 h + j, columns 16 m + 4 a .. + 4
+        const char* src = wbuf + (lg * 8 + (li >> 2)) * kDPitch + (m * 16 + (li & 3) * 4) * 2;
+        const s4_t r0 = lds_read_tr16(src), r1 = lds_read_tr16(src + 4 * kDPitch);
+        // (joined as one vector: element-wise extraction of these results miscompiles)
+        const h8_t fa = __builtin_bit_cast(h8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           acc[m][t] = mma(fa, fb_hi[t], acc[m][t]);
