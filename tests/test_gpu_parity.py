@@ -125,6 +125,35 @@ def test_edge_lists(label, B):
     check_y(y.cpu().numpy(), ob.sparse_ffn(xn, one), tol)
 
 
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_extreme_thresholds(label, B):
+    """No neuron above the threshold (empty list: y is zero, a residual is unchanged) and every
+    neuron above it (the full list 0..F-1: the layer is the dense FFN), through both the predictor
+    call and the one-call layer (which orders the list inside the FFN kernel)."""
+    c = setup_case(label)
+    say("extreme thresholds", label, "B", B)
+    x = c["X"][:B].contiguous()
+    F, d = c["spec"].F, c["spec"].d
+    for thr in (1e30, -1e30):
+        idx, cnt = ps.predict(c["P"], x, c["ws"], thr=thr)
+        n_exp = 0 if thr > 0 else F
+        assert int(cnt.item()) == n_exp
+        if n_exp:
+            assert torch.equal(idx.cpu(), torch.arange(F, dtype=torch.int32))
+        idx2, cnt2, y = ps.layer(c["P"], c["W"], x, c["ws"], thr=thr)
+        assert int(cnt2.item()) == n_exp
+        if n_exp == 0:
+            assert torch.count_nonzero(y).item() == 0
+            base = torch.randn(B, d, generator=torch.Generator().manual_seed(3)).to(DEV)
+            acc = base.clone()
+            ps.layer(c["P"], c["W"], x, c["ws"], thr=thr, y=acc, accumulate=True)
+            assert torch.equal(acc, base)
+        else:
+            assert torch.equal(idx2.cpu(), torch.arange(F, dtype=torch.int32))
+            check_y(y.cpu().numpy(), c["orc"].dense_ffn(c["Xn"][:B]), tol_for(c["spec"].storage))
+
+
 @pytest.mark.parametrize("label", ["f32_relu", "f16_relu", "i4_relu"])
 def test_perfect_predictor_list_gives_dense(label):
     c = setup_case(label)
