@@ -274,12 +274,15 @@ def test_layer_call_equals_two_calls_and_oracle(label, B):
     say("layer", label, "B", B)
     x = c["X"][:B].contiguous()
     F = c["spec"].F
-    idx1, cnt1 = ps.predict(c["P"], x, c["ws"])
+    logits1 = torch.empty(B, F, device=DEV)
+    idx1, cnt1 = ps.predict(c["P"], x, c["ws"], logits=logits1)
     y1 = ps.sparse_ffn(c["W"], x, idx1, cnt1, c["ws"])
     logits = torch.empty(B, F, device=DEV)
     idx2, cnt2, y2 = ps.layer(c["P"], c["W"], x, c["ws"], logits=logits)
     torch.cuda.synchronize()
     n = int(cnt1.item())
+    # the same logit arithmetic in both paths: the same logits, the same list
+    assert torch.equal(logits1, logits)
     assert int(cnt2.item()) == n and torch.equal(idx1[:n], idx2[:n])
     assert torch.equal(y1, y2)  # same kernels downstream of the list: bit-identical
     ref = oracle.predict_logits(c["n"]["A"], c["n"]["Q"], c["n"]["c"], c["Xn"][:B])
