@@ -67,6 +67,8 @@ def _L():
         _lib.orc_predict_logits.argtypes = [_i, _p, _p, _p, _i, _i, _i, _i, _p, _i, _p]
         _lib.orc_compact.restype = _i
         _lib.orc_compact.argtypes = [_p, _i, _i, _d, _p]
+        _lib.orc_compact_hot.restype = _i
+        _lib.orc_compact_hot.argtypes = [_p, _i, _i, _d, _i, _p]
         _lib.orc_activations.restype = None
         _lib.orc_activations.argtypes = [_i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p, _i, _p]
         _lib.orc_sparse_ffn.restype = None
@@ -159,12 +161,18 @@ def predict_logits(A, Q, c, x):
     return out
 
 
-def compact(logits, thr: float = 0.0):
-    """Ascending int32 list of neurons whose logit exceeds thr for at least one token."""
+def compact(logits, thr: float = 0.0, n_hot: int = 0):
+    """Ascending int32 list of neurons whose logit exceeds thr for at least one token.
+
+    n_hot > 0: the hot prefix [0, n_hot) of a hot-first layer is kept whatever its logits (the
+    predictor gates only the cold tail)."""
     logits = np.ascontiguousarray(np.atleast_2d(logits), dtype=np.float64)
     B, F = logits.shape
     idx = np.empty(F, dtype=np.int32)
-    n = _L().orc_compact(_ptr(logits), B, F, float(thr), _ptr(idx))
+    if n_hot:
+        n = _L().orc_compact_hot(_ptr(logits), B, F, float(thr), int(n_hot), _ptr(idx))
+    else:
+        n = _L().orc_compact(_ptr(logits), B, F, float(thr), _ptr(idx))
     return idx[:n].copy()
 
 

@@ -143,6 +143,22 @@ int orc_compact(const double* logits, int B, int F, double thr, int32_t* idx) {
   return n;
 }
 
+/* Hot prefix (Elamur summary, Summary 1st paragraph: a small set of hot neurons fires for
+ * almost every input; Interesting ideas, I1: place the most used parts first).  With the neurons
+ * in hot-first order, the first n_hot of them are kept for every batch without consulting the
+ * predictor; the predictor decides only for the rest (same rule as orc_compact).  Ascending
+ * order; returns the count. */
+int orc_compact_hot(const double* logits, int B, int F, double thr, int n_hot, int32_t* idx) {
+  int n = 0;
+  for (int i = 0; i < F; ++i) {
+    int on = i < n_hot;
+    for (int b = 0; b < B && !on; ++b)
+      if (logits[(size_t)b * F + i] > thr) on = 1;
+    if (on) idx[n++] = i;
+  }
+  return n;
+}
+
 /* Activation of neuron i for token b (Interesting ideas, I4: work on whole rows).
  *   ReLU  : a = max(W_up[i] . x + b_up[i], 0)
  *   SwiGLU: a = silu(W_gate[i] . x + b_gate[i]) * (W_up[i] . x + b_up[i]),  silu(g) = g / (1 + e^-g)

@@ -283,6 +283,22 @@ def test_fire_counts_match_numpy():
             assert np.array_equal(lay.fire_counts(X, t), (z > t).sum(axis=1).astype(np.int32))
 
 
+def test_compact_with_hot_prefix():
+    # the hot prefix [0, n_hot) is kept whatever the logits; the rest follows the strict rule
+    logits = rng.standard_normal((3, 400))
+    logits[:, :50] = -5.0  # a hot neuron the predictor would drop is still kept
+    for n_hot in (0, 1, 37, 64, 399, 400):
+        got = oracle.compact(logits, 0.0, n_hot=n_hot)
+        ref = sorted(set(range(n_hot)) | {i for i in range(400) if any(logits[b, i] > 0.0 for b in range(3))})
+        assert np.array_equal(got, np.array(ref, dtype=np.int32)), n_hot
+    assert np.array_equal(oracle.compact(logits, 0.0, n_hot=0), oracle.compact(logits, 0.0))
+    assert np.array_equal(oracle.compact(np.full((1, 9), -1.0), 0.0, n_hot=9), np.arange(9))
+    assert np.array_equal(oracle.compact(np.full((2, 9), -1.0), 0.0, n_hot=4), np.arange(4))
+    # the tail equals the plain rule on the tail
+    tail = oracle.compact(logits, 0.3, n_hot=120)
+    assert np.array_equal(tail[tail >= 120], np.flatnonzero(logits.max(axis=0) > 0.3)[np.flatnonzero(logits.max(axis=0) > 0.3) >= 120])
+
+
 def test_hot_first_perm_is_stable_descending_bijection():
     counts = rng.integers(0, 6, 3000).astype(np.int32)  # many ties
     perm = oracle.hot_first_perm(counts)
