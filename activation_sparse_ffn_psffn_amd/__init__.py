@@ -12,6 +12,7 @@ Calls mirror the C ABI by name:
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass, replace
 from typing import Optional
@@ -58,6 +59,10 @@ _lib.psffn_sparse_ffn.restype = _i
 _lib.psffn_sparse_ffn.argtypes = [_P(_FFN), _vp, _i, _vp, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.psffn_layer.restype = _i
 _lib.psffn_layer.argtypes = [_P(_Predictor), _P(_FFN), _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.psffn_predict_hot.restype = _i
+_lib.psffn_predict_hot.argtypes = [_P(_Predictor), _i, _vp, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.psffn_layer_hot.restype = _i
+_lib.psffn_layer_hot.argtypes = [_P(_Predictor), _P(_FFN), _i, _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.psffn_profile_counts.restype = _i
 _lib.psffn_profile_counts.argtypes = [_P(_FFN), _vp, _i, _vp, _vp]
 _lib.psffn_permute_hot_first.restype = _i
@@ -67,7 +72,8 @@ _lib.psffn_layernorm_f16.restype = _i
 _lib.psffn_layernorm_f16.argtypes = [_vp, _i, _i, _f, _vp, _vp]
 
 EXPORTED = ("psffn_status_str", "psffn_workspace_bytes", "psffn_workspace_init", "psffn_predict", "psffn_compact",
-            "psffn_sparse_ffn", "psffn_layer", "psffn_profile_counts", "psffn_permute_hot_first",
+            "psffn_sparse_ffn", "psffn_layer", "psffn_predict_hot", "psffn_layer_hot", "psffn_profile_counts",
+            "psffn_permute_hot_first",
             "psffn_layernorm_f16")
 
 
@@ -169,8 +175,11 @@ def new_workspace(P: Optional[Predictor], W: Optional[FFN], B: int, device="cuda
 
 
 def predict(P: Predictor, x: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, idx: torch.Tensor = None,
-            count: torch.Tensor = None, logits: torch.Tensor = None, stream=None):
-    """Active neurons of the batch x [B][d]: (idx int32 [F] ascending, count int32 [1]) on the device."""
+            count: torch.Tensor = None, logits: torch.Tensor = None, stream=None, n_hot: int = 0):
+    """Active neurons of the batch x [B][d]: (idx int32 [F] ascending, count int32 [1]) on the device.
+
+    n_hot > 0: the first n_hot neurons of a hot-first layer are listed without prediction
+    (psffn_predict_hot)."""
     B = x.shape[0]
     F = P.Q.shape[0]
     if idx is None:
@@ -178,6 +187,10 @@ def predict(P: Predictor, x: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, i
     if count is None:
         count = torch.empty(1, dtype=torch.int32, device=x.device)
     s = P.struct()
+    if n_hot:
+        _check(_lib.psffn_predict_hot(ctypes.byref(s), int(n_hot), _ptr(x), B, float(thr), _ptr(idx), _ptr(count),
+                                      _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)), "predict_hot")
+        return idx, count
     _check(_lib.psffn_predict(ctypes.byref(s), _ptr(x), B, float(thr), _ptr(idx), _ptr(count), _ptr(logits), _ptr(ws),
                               ws.numel(), _stream(stream)), "predict")
     return idx, count
@@ -207,8 +220,10 @@ def sparse_ffn(W: FFN, x: torch.Tensor, idx: torch.Tensor, count: torch.Tensor, 
 
 def layer(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, thr: float = 0.0, idx: torch.Tensor = None,
           count: torch.Tensor = None, logits: torch.Tensor = None, y: torch.Tensor = None, accumulate: bool = False,
-          stream=None):
-    """One decode step of one layer (predict + sparse FFN in one call): returns (idx, count, y)."""
+          stream=None, n_hot: int = 0):
+    """One decode step of one layer (predict + sparse FFN in one call): returns (idx, count, y).
+
+    n_hot > 0: hot prefix as in predict (psffn_layer_hot)."""
     B = x.shape[0]
     F = P.Q.shape[0]
     if idx is None:
@@ -218,6 +233,11 @@ def layer(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, thr: float = 
     if y is None:
         y = torch.empty(B, W.d, dtype=torch.float32, device=x.device)
     sp, sw = P.struct(), W.struct()
+    if n_hot:
+        _check(_lib.psffn_layer_hot(ctypes.byref(sp), ctypes.byref(sw), int(n_hot), _ptr(x), B, float(thr), _ptr(idx),
+                                    _ptr(count), _ptr(logits), _ptr(y), int(bool(accumulate)), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "layer_hot")
+        return idx, count, y
     _check(_lib.psffn_layer(ctypes.byref(sp), ctypes.byref(sw), _ptr(x), B, float(thr), _ptr(idx), _ptr(count),
                             _ptr(logits), _ptr(y), int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream)),
            "layer")
@@ -256,3 +276,17 @@ def layernorm_f16(x: torch.Tensor, eps: float = 1e-5, out: torch.Tensor = None, 
         out = torch.empty(B, d, dtype=torch.float16, device=x.device)
     _check(_lib.psffn_layernorm_f16(_ptr(x), B, d, float(eps), _ptr(out), _stream(stream)), "layernorm_f16")
     return out
+
+
+def hot_prefix_len(counts: torch.Tensor, tokens: int, p_hot: float) -> int:
+    """Length of the hot prefix of a hot-first layer: the number of neurons whose profiled firing
+    frequency counts[i] / tokens is at least p_hot.  counts are the profile counts in the layer's
+    (hot-first) order, so these neurons are exactly the first ones."""
+    if tokens < 1 or not (0.0 < p_hot <= 1.0):
+        raise ValueError("hot_prefix_len: tokens >= 1 and 0 < p_hot <= 1")
+    c = counts.detach().to("cpu", torch.int64)
+    need = math.ceil(p_hot * tokens - 1e-9)
+    n = int((c >= need).sum().item())
+    if n and int(c[:n].min().item()) < need:
+        raise ValueError("hot_prefix_len: counts are not in hot-first (descending) order")
+    return n

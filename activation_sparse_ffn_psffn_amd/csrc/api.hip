@@ -127,8 +127,15 @@ psffn_status psffn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream)
 
 psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float logit_thr, int32_t* idx,
                            int32_t* count, float* logits, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return psffn_predict_hot(P, 0, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
+}
+
+psffn_status psffn_predict_hot(const psffn_predictor* P, int n_hot, const void* x, int B, float logit_thr,
+                               int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
   psffn_status st = check_pred(P);
   if (st != PSFFN_OK) return st;
+  if (n_hot < 0 || n_hot > P->F) return PSFFN_E_INVALID_ARG;
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) ||
       (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
     return PSFFN_E_INVALID_ARG;
@@ -137,16 +144,16 @@ psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float
   const St pt = st_of(P->dt);
   hipError_t e = hipErrorNotSupported;
   if (B <= kFusedMaxBatch)
-    e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream);
+    e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream, n_hot);
   else
-    e = launch_predict_batch(*P, x, B, logit_thr, idx, count, logits, ws, stream);
+    e = launch_predict_batch(*P, x, B, logit_thr, idx, count, logits, ws, stream, n_hot);
   if (e == hipErrorNotSupported) {
     char* base = static_cast<char*>(ws) + state_layout(P->F).scratch;
     float* h = reinterpret_cast<float*>(base);
     uint8_t* flags = reinterpret_cast<uint8_t*>(base + round256((size_t)B * P->r * 4));
     e = launch_pred_h(pt, P->A, x, B, P->d, P->r, h, stream);
     if (e == hipSuccess) e = launch_pred_logits(pt, P->Q, P->c, h, B, P->r, P->F, logit_thr, logits, flags, stream);
-    if (e == hipSuccess) e = launch_scatter(flags, P->F, idx, count, stream);
+    if (e == hipSuccess) e = launch_scatter(flags, P->F, idx, count, stream, n_hot);
   }
   return hip_status(e);
 }
@@ -193,9 +200,16 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
 psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B, float logit_thr,
                          int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
+  return psffn_layer_hot(P, W, 0, x, B, logit_thr, idx, count, logits, y, accumulate, ws, ws_bytes, stream);
+}
+
+psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n_hot, const void* x, int B,
+                             float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y, int accumulate,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
   psffn_status st = check_pred(P);
   if (st == PSFFN_OK) st = check_ffn(W);
   if (st != PSFFN_OK) return st;
+  if (n_hot < 0 || n_hot > P->F) return PSFFN_E_INVALID_ARG;
   if (P->F != W->F || P->d != W->d) return PSFFN_E_INVALID_ARG;
   if ((P->dt == PSFFN_F32) != (W->dt == PSFFN_F32)) return PSFFN_E_UNSUPPORTED;
   if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
@@ -208,12 +222,12 @@ psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const voi
   if (st != PSFFN_OK) return st;
   hipError_t e = hipErrorNotSupported;
   if (B <= kFusedMaxBatch)
-    e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
+    e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
   else
-    e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream);
+    e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
   if (e != hipErrorNotSupported) return hip_status(e);
   // shapes outside the one-call path: the two calls, same results
-  st = psffn_predict(P, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
+  st = psffn_predict_hot(P, n_hot, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
   if (st != PSFFN_OK) return st;
   return psffn_sparse_ffn(W, x, B, idx, count, y, accumulate, ws, ws_bytes, stream);
 }

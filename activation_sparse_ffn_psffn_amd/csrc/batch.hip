@@ -109,6 +109,7 @@ struct BArgs {
   uint16_t* hlo;
   uint32_t* masks;
   int nq;
+  int n_hot;  // hot prefix: neurons [0, n_hot) are listed whatever their logits
   int32_t* idx_out;
   int32_t* count_out;
   // shared
@@ -160,14 +161,20 @@ __device__ __forceinline__ void bsplit(int n, int B, int d, int row_bytes, int c
 
 // ---- list ordering from mask words (bit b of word q: neuron 32q + b is active) ----------------
 template <int NTH>
-__device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, uint32_t* s_mask, int* s_pre, int* s_red) {
+__device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, int n_hot, uint32_t* s_mask, int* s_pre,
+                            int* s_red) {
   for (int q0 = threadIdx.x; q0 < nq; q0 += 8 * NTH) {
     uint32_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = q0 + u * NTH < nq ? masks[q0 + u * NTH] : 0u;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (q0 + u * NTH < nq) s_mask[q0 + u * NTH] = v[u];
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u * NTH;
+      // the hot prefix's bits (n_hot <= F, so no bit past F is set)
+      const int nh = n_hot - 32 * q;
+      const uint32_t hot = nh >= 32 ? 0xffffffffu : (nh > 0 ? (1u << nh) - 1u : 0u);
+      if (q < nq) s_mask[q] = v[u] | hot;
+    }
   }
   __syncthreads();
   const int per = (nq + NTH - 1) / NTH;  // consecutive words per thread
@@ -637,7 +644,7 @@ __global__ __launch_bounds__(kScanThreads) void k_bscan(BArgs g) {
   uint32_t* s_mask = s_dyn;
   int* s_pre = reinterpret_cast<int*>(s_dyn + g.nq);
   __shared__ int s_red[kScanThreads / kWave];
-  mask_prefix<kScanThreads>(g.masks, g.nq, s_mask, s_pre, s_red);
+  mask_prefix<kScanThreads>(g.masks, g.nq, g.n_hot, s_mask, s_pre, s_red);
   const int total = min(s_pre[g.nq], g.F);
   if (threadIdx.x == 0) *g.count_out = total;
   for (int q = threadIdx.x; q < g.nq; q += kScanThreads) {
@@ -1332,10 +1339,11 @@ static hipError_t predict_and_scan(const BArgs& g, hipStream_t s) {
 }
 
 hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
-                                int32_t* count, float* logits, void* ws, hipStream_t s) {
+                                int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot) {
   if (!batch_supported_pred(P, B)) return hipErrorNotSupported;
   BArgs g{};
   pred_args(g, P, x, B, thr, logits, ws);
+  g.n_hot = n_hot;
   g.idx_out = idx;
   g.count_out = count;
   const hipError_t e = predict_and_scan(g, s);
@@ -1353,10 +1361,11 @@ hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int3
 
 hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, int n_hot) {
   if (!batch_supported_pred(P, B) || !batch_supported_ffn(W, B)) return hipErrorNotSupported;
   BArgs g{};
   pred_args(g, P, x, B, thr, logits, ws);
+  g.n_hot = n_hot;
   g.idx_out = idx;
   g.count_out = count;
   hipError_t e = predict_and_scan(g, s);

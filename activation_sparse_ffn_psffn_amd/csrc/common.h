@@ -137,7 +137,7 @@ hipError_t launch_pred_h(St st, const void* A, const void* x, int B, int d, int 
 hipError_t launch_pred_logits(St st, const void* Q, const float* c, const float* h, int B, int r, int F, float thr,
                               float* logits, uint8_t* flags, hipStream_t s);
 hipError_t launch_flags_from_logits(const float* logits, int B, int F, float thr, uint8_t* flags, hipStream_t s);
-hipError_t launch_scatter(const uint8_t* flags, int F, int32_t* idx, int32_t* count, hipStream_t s);
+hipError_t launch_scatter(const uint8_t* flags, int F, int32_t* idx, int32_t* count, hipStream_t s, int n_hot = 0);
 hipError_t launch_up(St st, psffn_act act, const psffn_ffn& W, const void* x, int B, const int32_t* idx,
                      const int32_t* count, float* a, hipStream_t s);
 hipError_t launch_down(St st, const psffn_ffn& W, const float* a, int B, const int32_t* idx, const int32_t* count,
@@ -156,13 +156,14 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 // They return hipErrorNotSupported when the shape is outside what they handle, and the caller
 // takes the generic kernels.
 constexpr int kFusedMaxBatch = 4;
+// n_hot: neurons [0, n_hot) are listed whatever their logits (0 <= n_hot <= F)
 hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
-                                int32_t* count, float* logits, void* ws, hipStream_t s);
+                                int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot = 0);
 hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
                             float* y, int accumulate, void* ws, hipStream_t s);
 hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s);
+                              hipStream_t s, int n_hot = 0);
 
 // batch pipeline (kFusedMaxBatch < B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA
 // tiles; the same NotSupported convention
@@ -170,12 +171,12 @@ bool batch_supported_pred(const psffn_predictor& P, int B);
 bool batch_supported_ffn(const psffn_ffn& W, int B);
 size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_act act, bool pred, bool ffn);
 hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
-                                int32_t* count, float* logits, void* ws, hipStream_t s);
+                                int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot = 0);
 hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
                             float* y, int accumulate, void* ws, hipStream_t s);
 hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s);
+                              hipStream_t s, int n_hot = 0);
 
 }  // namespace psffn
 

@@ -120,18 +120,39 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
 // =========================================================================================
 // k_q: chunk q = blockIdx.x covers neurons [q*4*RPW, (q+1)*4*RPW), RPW per wave.  All Q row
 // loads are issued first; h (fp32, from the previous kernel) is read next; then logits, the
-// union test over the batch, and the chunk's mask bits.
+// union test over the batch, and the chunk's mask bits.  Neurons below n_hot (the hot prefix of a
+// hot-first layer) are kept without a test: their Q rows are not read, their bits are set, and
+// their logits are left unspecified.
+
+// The chunk's active bits.  Chunks of 16 neurons write the halves of the 32-bit words (little
+// endian); an odd last chunk writes its whole word, so the unused upper half reads as zero.
+template <int ROWS>
+__device__ __forceinline__ void store_chunk_bits(uint32_t* masks, int q, int NQ, uint32_t bits) {
+  static_assert(ROWS == 32 || ROWS == 16, "chunks of 32 or 16 neurons");
+  if constexpr (ROWS == 32) {
+    masks[q] = bits;
+  } else if ((q & 1) == 0 && q == NQ - 1) {
+    masks[q >> 1] = bits;
+  } else {
+    reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
+  }
+}
 
 template <St PT, int NB, int RV, int RPW>
 __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const float* __restrict__ c,
                                               const float* __restrict__ h, int r, int F, float thr, int nb,
-                                              float* __restrict__ logits, int NQ, uint32_t* __restrict__ masks) {
+                                              float* __restrict__ logits, int NQ, uint32_t* __restrict__ masks,
+                                              int n_hot) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int ROWS = 4 * RPW;
   __shared__ uint32_t s_mask[kBlock / kWave];
   const int lane = wave_lane(), wv = wave_id();
   const int q = blockIdx.x;
+  if ((q + 1) * ROWS <= n_hot) {  // the whole chunk is hot (and below F)
+    if (threadIdx.x == 0) store_chunk_bits<ROWS>(masks, q, NQ, ROWS == 32 ? 0xffffffffu : 0xffffu);
+    return;
+  }
   const int i0 = q * ROWS + wv * RPW;
   uint4 qv[RPW][RV];
 #pragma unroll
@@ -139,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
 #pragma unroll
     for (int v = 0; v < RV; ++v) {
       const int i = i0 + k, e = v * kWave * EPL + lane * EPL;
-      qv[k][v] = ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && e < r);
+      qv[k][v] = ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && i >= n_hot && e < r);
     }
   float hv[NB][RV][EPL];
 #pragma unroll
@@ -186,23 +207,13 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
         if (logits && lane == 0 && i < F) logits[(size_t)b * F + i] = l;
       }
     }
-    if (on && i < F) mask |= 1u << k;
+    if ((on || i < n_hot) && i < F) mask |= 1u << k;
   }
   if (lane == 0) s_mask[wv] = mask;
   __syncthreads();
-  // the chunk's active bits.  Chunks of 16 neurons write the halves of the 32-bit words (little
-  // endian); an odd last chunk writes its whole word, so the unused upper half reads as zero.
-  static_assert(4 * RPW == 32 || 4 * RPW == 16, "chunks of 32 or 16 neurons");
-  if (threadIdx.x == 0) {
-    const uint32_t bits = s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW));
-    if constexpr (4 * RPW == 32) {
-      masks[q] = bits;
-    } else if ((q & 1) == 0 && q == NQ - 1) {
-      masks[q >> 1] = bits;
-    } else {
-      reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
-    }
-  }
+  if (threadIdx.x == 0)
+    store_chunk_bits<ROWS>(masks, q, NQ,
+                           s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW)));
 }
 
 // =========================================================================================
@@ -959,7 +970,7 @@ __global__ __launch_bounds__(kBlock) void k_reduce_ud(FfnArgs g) {
 
 template <St PT, int NB, int RV>
 static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx, int32_t* count,
-                            float* logits, void* ws, hipStream_t s) {
+                            float* logits, void* ws, hipStream_t s, int n_hot) {
   constexpr int RPW = 4;               // k_q chunks of 16 neurons
   const int NC = (P.F + 4 * RPW - 1) / (4 * RPW);
   const int NQ = (P.F + 31) / 32;      // 32-bit mask words
@@ -970,36 +981,36 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
-  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
+  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
   k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
   return hipGetLastError();
 }
 
 template <St PT, int NB>
 static hipError_t predict_rv(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx, int32_t* count,
-                             float* logits, void* ws, hipStream_t s) {
+                             float* logits, void* ws, hipStream_t s, int n_hot) {
   const int per = kWave * Tr<PT>::EPL;  // elements of a row covered by one 16-byte slice per lane
   const int rv = (P.r + per - 1) / per;
-  if (rv == 1) return predict_t<PT, NB, 1>(P, x, B, thr, idx, count, logits, ws, s);
-  if (rv == 2) return predict_t<PT, NB, 2>(P, x, B, thr, idx, count, logits, ws, s);
-  if (rv == 3) return predict_t<PT, NB, 3>(P, x, B, thr, idx, count, logits, ws, s);
-  if (rv == 4) return predict_t<PT, NB, 4>(P, x, B, thr, idx, count, logits, ws, s);
+  if (rv == 1) return predict_t<PT, NB, 1>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (rv == 2) return predict_t<PT, NB, 2>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (rv == 3) return predict_t<PT, NB, 3>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (rv == 4) return predict_t<PT, NB, 4>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 
 template <St PT>
 static hipError_t predict_nb(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx, int32_t* count,
-                             float* logits, void* ws, hipStream_t s) {
-  if (B == 1) return predict_rv<PT, 1>(P, x, B, thr, idx, count, logits, ws, s);
-  if (B == 2) return predict_rv<PT, 2>(P, x, B, thr, idx, count, logits, ws, s);
-  if (B <= 4) return predict_rv<PT, 4>(P, x, B, thr, idx, count, logits, ws, s);
+                             float* logits, void* ws, hipStream_t s, int n_hot) {
+  if (B == 1) return predict_rv<PT, 1>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (B == 2) return predict_rv<PT, 2>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (B <= 4) return predict_rv<PT, 4>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 
 hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
-                                int32_t* count, float* logits, void* ws, hipStream_t s) {
-  if (st == St::F32) return predict_nb<St::F32>(P, x, B, thr, idx, count, logits, ws, s);
-  if (st == St::F16) return predict_nb<St::F16>(P, x, B, thr, idx, count, logits, ws, s);
+                                int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot) {
+  if (st == St::F32) return predict_nb<St::F32>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
+  if (st == St::F16) return predict_nb<St::F16>(P, x, B, thr, idx, count, logits, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 
@@ -1098,7 +1109,8 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
 
 template <St PT, St WT, psffn_act ACT, int NB, int RV>
 static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
-                          int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
+                          int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
+                          int n_hot) {
   constexpr int RPW = 4;                  // k_q chunks of 16 neurons (32 KB of Q rows in flight each)
   const int NQ = (P.F + 31) / 32;         // 32-bit mask words
   const int NC = (P.F + 4 * RPW - 1) / (4 * RPW);
@@ -1114,7 +1126,7 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
-  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks);
+  k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
   FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
   g.masks = masks;
   g.nq = NQ;
@@ -1125,42 +1137,45 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
 
 template <St PT, St WT, psffn_act ACT, int NB>
 static hipError_t layer_rv(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
-                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
+                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
+                           int n_hot) {
   const int per = kWave * Tr<PT>::EPL;
   const int rv = (P.r + per - 1) / per;
-  if (rv == 1) return layer_t<PT, WT, ACT, NB, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  if (rv == 2) return layer_t<PT, WT, ACT, NB, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  if (rv == 3) return layer_t<PT, WT, ACT, NB, 3>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  if (rv == 4) return layer_t<PT, WT, ACT, NB, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+  if (rv == 1) return layer_t<PT, WT, ACT, NB, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (rv == 2) return layer_t<PT, WT, ACT, NB, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (rv == 3) return layer_t<PT, WT, ACT, NB, 3>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (rv == 4) return layer_t<PT, WT, ACT, NB, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 
 template <St PT, St WT, psffn_act ACT>
 static hipError_t layer_nb(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
-                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s) {
-  if (B == 1) return layer_rv<PT, WT, ACT, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  if (B == 2) return layer_rv<PT, WT, ACT, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  if (B <= 4) return layer_rv<PT, WT, ACT, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
+                           int n_hot) {
+  if (B == 1) return layer_rv<PT, WT, ACT, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (B == 2) return layer_rv<PT, WT, ACT, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (B <= 4) return layer_rv<PT, WT, ACT, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 
 template <St PT, St WT>
 static hipError_t layer_act(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                             int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                            hipStream_t s) {
-  if (W.act == PSFFN_RELU) return layer_nb<PT, WT, PSFFN_RELU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
-  return layer_nb<PT, WT, PSFFN_SWIGLU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+                            hipStream_t s, int n_hot) {
+  if (W.act == PSFFN_RELU)
+    return layer_nb<PT, WT, PSFFN_RELU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  return layer_nb<PT, WT, PSFFN_SWIGLU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
 }
 
 hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, int n_hot) {
   if (P.dt == PSFFN_F32 && W.dt == PSFFN_F32)
-    return layer_act<St::F32, St::F32>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+    return layer_act<St::F32, St::F32>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
   if (P.dt == PSFFN_F16 && W.dt == PSFFN_F16)
-    return layer_act<St::F16, St::F16>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+    return layer_act<St::F16, St::F16>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
   if (P.dt == PSFFN_F16 && W.dt == PSFFN_I4G128)
-    return layer_act<St::F16, St::I4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s);
+    return layer_act<St::F16, St::I4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
   return hipErrorNotSupported;
 }
 

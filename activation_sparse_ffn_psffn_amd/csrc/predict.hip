@@ -96,7 +96,7 @@ __global__ __launch_bounds__(kBlock) void k_flags_from_logits(const float* __res
 
 // Ordered compaction: chunk c (256 neurons) counts the active flags of all earlier chunks, then
 // each wave ranks its lanes with ballot + mbcnt.  The last chunk writes the total count.
-__global__ __launch_bounds__(kBlock) void k_scatter(const uint8_t* __restrict__ flags, int F,
+__global__ __launch_bounds__(kBlock) void k_scatter(const uint8_t* __restrict__ flags, int F, int n_hot,
                                                     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   __shared__ int s_red[kBlock / kWave];
   __shared__ int s_wc[kBlock / kWave];
@@ -107,12 +107,13 @@ __global__ __launch_bounds__(kBlock) void k_scatter(const uint8_t* __restrict__ 
   const uint32_t* f4 = reinterpret_cast<const uint32_t*>(flags);
   for (int w = threadIdx.x; w < nbytes / 4; w += kBlock) {
     uint32_t v = f4[w];
-    pre += (int)((v & 1u) + ((v >> 8) & 1u) + ((v >> 16) & 1u) + ((v >> 24) & 1u));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pre += (int)(((v >> (8 * k)) & 1u) | (uint32_t)(4 * w + k < n_hot));
   }
   float ps = wave_sum((float)pre);  // exact: counts < 2^24
   if (lane == 0) s_red[wv] = (int)ps;
   const int i = c * kBlock + threadIdx.x;
-  const bool on = i < F && flags[i] != 0;
+  const bool on = i < F && (i < n_hot || flags[i] != 0);
   const unsigned long long bal = __ballot(on);
   const int rank = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
   if (lane == 0) s_wc[wv] = __popcll(bal);
@@ -176,8 +177,8 @@ hipError_t launch_flags_from_logits(const float* logits, int B, int F, float thr
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const uint8_t* flags, int F, int32_t* idx, int32_t* count, hipStream_t s) {
-  k_scatter<<<(F + kBlock - 1) / kBlock, kBlock, 0, s>>>(flags, F, idx, count);
+hipError_t launch_scatter(const uint8_t* flags, int F, int32_t* idx, int32_t* count, hipStream_t s, int n_hot) {
+  k_scatter<<<(F + kBlock - 1) / kBlock, kBlock, 0, s>>>(flags, F, n_hot, idx, count);
   return hipGetLastError();
 }
 

@@ -61,12 +61,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(spec, B, n_active):
-    """Bytes the method must move for one step with n_active listed neurons (per-step mean)."""
+def algorithmic_bytes(spec, B, n_active, n_hot=0):
+    """Bytes the method must move for one step with n_active listed neurons (per-step mean).
+    With a hot prefix (B <= 4) the predictor reads the Q rows and biases of the other F - n_hot
+    neurons only."""
     e_p = 4 if spec.storage == "f32" else 2
     e_x = 4 if spec.storage == "f32" else 2
     d, F, r = spec.d, spec.F, spec.r
-    pred = (r * d + F * r) * e_p + 4 * F + B * d * e_x
+    Fq = F - n_hot if B <= 4 else F
+    pred = (r * d + Fq * r) * e_p + 4 * Fq + B * d * e_x
     if spec.storage == "i4":
         rowb = d // 2 + 2 * (d // 128)
     else:
@@ -91,6 +94,14 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 8 times with a plain device copy and exit (reference "
                          "kernel of known traffic for scaling hardware byte counters)")
+    ap.add_argument("--hot", type=float, default=0.0, metavar="P_HOT",
+                    help="hot prefix: neurons profiled to fire on at least this fraction of the profile tokens "
+                         "are computed without prediction (psffn_layer_hot); the layer is profiled and permuted "
+                         "hot-first first.  0 = off")
+    ap.add_argument("--study", default="", choices=["", "predictor"],
+                    help="predictor: accuracy and speed of predictors aligned with the layer (rank-r "
+                         "approximations of the deciding weights) at several ranks, against the generated one")
+    ap.add_argument("--ranks", default="128,256,512,1024", help="ranks of the aligned predictors (--study)")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="steps per captured HIP graph in the timed region (0: eager launches)")
     args = ap.parse_args()
@@ -121,6 +132,8 @@ def main():
     B = args.batch
     dev = "cuda"
     torch.cuda.init()
+    if args.study == "predictor":
+        return bench_study(args, spec, ps, synth, np, torch)
     if spec.layers > 1:
         return bench_stack(args, spec, ps, synth, np, torch)
     log("workload", spec.name, "B", B)
@@ -129,10 +142,15 @@ def main():
     W = ps.FFN(spec.act, L.w_up, L.w_dT, w_gate=L.w_gate, s_up=L.s_up, s_gate=L.s_gate, s_dT=L.s_dT, b_up=L.b_up,
                b_gate=L.b_gate, b_down=L.b_down)
     P = ps.Predictor(L.A, L.Q, L.c)
-    if spec.hot_first:
-        Xp = synth.make_tokens(spec, spec.profile_tokens, seed=0, stream="profile", device=dev)
+    n_hot = 0
+    if spec.hot_first or args.hot > 0:
+        T = spec.profile_tokens or 512
+        Xp = synth.make_tokens(spec, T, seed=0, stream="profile", device=dev)
         counts = ps.profile_counts(W, Xp)
         perm, W, P = ps.permute_hot_first(counts, W, P)
+        if args.hot > 0:
+            n_hot = ps.hot_prefix_len(counts[perm.long()], T, args.hot)
+            log("hot prefix: %d neurons fire on >= %.3f of %d profile tokens" % (n_hot, args.hot, T))
         del Xp, L
     torch.cuda.synchronize()
     log("layer ready in %.1f s" % (time.time() - t0))
@@ -158,7 +176,7 @@ def main():
     def step(t, cnt, stream):
         # one decode step of one layer: predict + sparse FFN in one library call
         Wc, Pc = copies[t % len(copies)]
-        ps.layer(Pc, Wc, X[t % ntok], ws, idx=idx, count=cnt, y=y, stream=stream)
+        ps.layer(Pc, Wc, X[t % ntok], ws, idx=idx, count=cnt, y=y, stream=stream, n_hot=n_hot)
 
     scratch_cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     for t in range(Wm):
@@ -202,7 +220,7 @@ def main():
 
     counts_np = counts_all.cpu().numpy().astype(np.float64)
     n_mean = float(counts_np.mean())
-    pred_bytes, ffn_bytes = algorithmic_bytes(spec, B, n_mean)
+    pred_bytes, ffn_bytes = algorithmic_bytes(spec, B, n_mean, n_hot)
     step_bytes = pred_bytes + ffn_bytes
     layer_gbps = step_bytes / (us_per_step * 1e-6) / 1e9
 
@@ -221,7 +239,8 @@ def main():
             with torch.cuda.graph(g_pred, stream=cap):
                 for t in range(K):
                     Wc, Pc = copies[(Wm + t) % len(copies)]
-                    ps.predict(Pc, X[(Wm + t) % ntok], ws, idx=idx_all[t], count=cnt_all[t:t + 1], stream=cap)
+                    ps.predict(Pc, X[(Wm + t) % ntok], ws, idx=idx_all[t], count=cnt_all[t:t + 1], stream=cap,
+                               n_hot=n_hot)
             with torch.cuda.graph(g_ffn, stream=cap):
                 for t in range(K):
                     Wc, Pc = copies[(Wm + t) % len(copies)]
@@ -244,7 +263,7 @@ def main():
         achieved = pred_bytes / (pred_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(spec.name, B),
+                "traffic": measured_traffic(spec.name, B) if not n_hot else None,
                 "kernel": "psffn_predict (k_h, k_q, k_list at B <= 4; the batch predictor kernels above): the "
                           "fp16 predictor stream A then Q, threshold, mask words, ordered list",
                 "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
@@ -260,8 +279,9 @@ def main():
         "vs_baseline": None, "dtype": "f16" if spec.storage != "f32" else "f32", "data": "synthetic",
         "config": {"workload": "%s: d=%d F=%d r=%d %s %s batch %d, Zipf(%.1f) density %.2f%s, %d layer copies" % (
             spec.name, spec.d, spec.F, spec.r, spec.storage, spec.act, B, spec.zipf, spec.density,
-            ", hot-first" if spec.hot_first else "", len(copies)), "batch": B, "d": spec.d, "F": spec.F,
-            "r": spec.r},
+            ", hot-first" if (spec.hot_first or n_hot) else "", len(copies)) + (
+            ", hot prefix of %d neurons (profiled firing >= %g) computed without prediction" % (n_hot, args.hot)
+            if n_hot else ""), "batch": B, "d": spec.d, "F": spec.F, "r": spec.r, "n_hot": n_hot},
         "layer": {"gbps": round(layer_gbps, 1), "frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
                   "algorithmic_bytes_per_step": int(step_bytes), "mean_active": round(n_mean, 2),
                   "tokens_per_s": round(1e6 / us_per_step * B, 1), "breakdown": breakdown},
@@ -334,6 +354,98 @@ def bench_stack(args, spec, ps, synth, np, torch):
                      "algorithmic_bytes_per_step": int(byt)},
            "roofline": None, "cpu_baseline": None}
     print(json.dumps(out), flush=True)
+
+
+def set_stats(pred_idx, fired):
+    """Recall and precision of a predicted neuron list against the truly firing set (bool [F])."""
+    import numpy as np
+    hit = int(fired[pred_idx].sum()) if len(pred_idx) else 0
+    nf, npred = int(fired.sum()), len(pred_idx)
+    return (hit / nf if nf else 1.0), (hit / npred if npred else 1.0)
+
+
+def cosine(a, b):
+    import numpy as np
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    na, nb = np.linalg.norm(a), np.linalg.norm(b)
+    return float(a @ b / (na * nb)) if na > 0 and nb > 0 else float(na == nb)
+
+
+def bench_study(args, spec, ps, synth, np, torch):
+    """Predictor accuracy against predictor size (one layer, batch 1).
+
+    For the generated predictor (independent of the weights, equal firing rates) and for
+    predictors aligned with the layer at each rank of --ranks (synth.make_aligned_predictor):
+    recall and precision of the predicted set against the neurons that truly fire (the ReLU or
+    gate pre-activation > 0, from psffn_profile_counts on each token alone), the cosine between the
+    predicted-set output and the dense FFN output (psffn_sparse_ffn over every neuron), and the
+    layer time (psffn_layer, graph replay over 8 rotating copies of the layer).  Every step runs
+    in the library's kernels; the statistics are host arithmetic on their outputs."""
+    dev = "cuda"
+    t0 = time.time()
+    L = synth.make_layer(spec, seed=0, device=dev)
+    W = ps.FFN(spec.act, L.w_up, L.w_dT, w_gate=L.w_gate, b_up=L.b_up, b_gate=L.b_gate, b_down=L.b_down)
+    F, d = spec.F, spec.d
+    T = min(64, spec.tokens)
+    X = synth.make_tokens(spec, T, seed=0, device=dev).reshape(T, 1, d)
+    ws = ps.new_workspace(ps.Predictor(L.A, L.Q, L.c), W, 1)
+    all_idx = torch.arange(F, dtype=torch.int32, device=dev)
+    all_cnt = torch.tensor([F], dtype=torch.int32, device=dev)
+    fired, dense = [], []
+    for t in range(T):
+        fired.append(ps.profile_counts(W, X[t]).cpu().numpy() > 0)
+        dense.append(ps.sparse_ffn(W, X[t], all_idx, all_cnt, ws).cpu().numpy())
+    log("layer and dense outputs ready in %.1f s" % (time.time() - t0))
+    variants = [("generated", spec.r, (L.A, L.Q, L.c))]
+    for r in [int(v) for v in args.ranks.split(",") if v]:
+        variants.append(("aligned", r, synth.make_aligned_predictor(L, r)))
+    esz = 4 if spec.storage == "f32" else 2
+    copies_w = [W] + [ps.FFN(spec.act, L.w_up.clone(), L.w_dT.clone(), w_gate=None if L.w_gate is None else
+                             L.w_gate.clone(), b_up=L.b_up, b_gate=L.b_gate) for _ in range(7)]
+    rows = []
+    for kind, r, (A, Q, c) in variants:
+        P = ps.Predictor(A, Q, c)
+        rec, prec, cos, nact = [], [], [], []
+        for t in range(T):
+            idx, cnt, y = ps.layer(P, W, X[t], ws)
+            n = int(cnt.item())
+            rc, pr = set_stats(idx[:n].cpu().numpy(), fired[t])
+            rec.append(rc)
+            prec.append(pr)
+            cos.append(cosine(y.cpu().numpy(), dense[t]))
+            nact.append(n)
+        # timing: 8 rotating copies (FFN weights and predictor), graph replay of K steps
+        Ps = [P] + [ps.Predictor(A.clone(), Q.clone(), c.clone()) for _ in range(7)]
+        K = 256
+        idx = torch.empty(F, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+        y = torch.empty(1, d, dtype=torch.float32, device=dev)
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gr, stream=cap):
+                for k in range(K):
+                    ps.layer(Ps[k % 8], copies_w[k % 8], X[k % T], ws, idx=idx, count=cnt, y=y, stream=cap)
+        torch.cuda.current_stream().wait_stream(cap)
+        gr.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / K
+        del gr, Ps
+        row = {"predictor": kind, "rank": r, "predictor_bytes": (r * d + F * r) * esz + 4 * F,
+               "recall": round(float(np.mean(rec)), 4), "precision": round(float(np.mean(prec)), 4),
+               "cosine_vs_dense": round(float(np.mean(cos)), 5), "mean_listed": round(float(np.mean(nact)), 1),
+               "mean_firing": round(float(np.mean([f.sum() for f in fired])), 1), "us_per_layer": round(us, 3)}
+        log(json.dumps(row))
+        rows.append(row)
+    print(json.dumps({"study": "predictor accuracy against rank", "workload": spec.name, "tokens": T, "batch": 1,
+                      "rows": rows}), flush=True)
 
 
 def cpu_baseline(spec, copy0, X, B, ntok):

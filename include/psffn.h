@@ -146,6 +146,22 @@ psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const voi
                          int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* Hot prefix (Elamur summary, Summary 1st paragraph: a small set of "hot" neurons fires for
+ * most inputs; Interesting ideas, I1: the most used parts go first).  In a hot-first layer
+ * (psffn_permute_hot_first) the neurons [0, n_hot) are listed for every batch without consulting
+ * the predictor, which decides only for [n_hot, F).  The list is the ascending union of the two.
+ *   n_hot   0 <= n_hot <= F (E_INVALID_ARG otherwise); 0 gives psffn_predict / psffn_layer exactly
+ *   logits  as psffn_predict for neurons >= n_hot; the entries of hot neurons are unspecified
+ * At B <= 4 the predictor does not read the Q rows of the hot prefix (F-n_hot rows stream
+ * instead of F); larger batches compute every logit and force the prefix into the list.
+ * Everything else (arguments, outputs, workspace, errors) is as in psffn_predict / psffn_layer. */
+psffn_status psffn_predict_hot(const psffn_predictor* P, int n_hot, const void* x, int B, float logit_thr,
+                               int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n_hot, const void* x, int B,
+                             float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y, int accumulate,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Offline activation profile (Summary, 2nd paragraph: models are profiled offline):
  * counts[i] = number of the T tokens X [T][d] for which neuron i truly fires -- the ReLU
  * pre-activation W_up[i].x + b_up[i] > 0, or for SwiGLU the gate W_gate[i].x + b_gate[i] > 0.

@@ -43,8 +43,9 @@ def spec_variant(name: str, **kw):
     return replace(synth.CONFIGS[name], **kw)
 
 
-def check_set(idx, count, logits_ref, thr=0.0):
-    """GPU list (idx tensor, count tensor) against oracle logits [B][F]; returns stats."""
+def check_set(idx, count, logits_ref, thr=0.0, n_hot=0):
+    """GPU list (idx tensor, count tensor) against oracle logits [B][F]; returns stats.
+    n_hot: the first n_hot neurons must be listed whatever their logits."""
     F = logits_ref.shape[1]
     n = int(count.cpu()[0])
     assert 0 <= n <= F
@@ -52,8 +53,9 @@ def check_set(idx, count, logits_ref, thr=0.0):
     assert np.all(np.diff(got_idx) > 0), "list not strictly ascending"
     assert n == 0 or (got_idx[0] >= 0 and got_idx[-1] < F)
     m = logits_ref.max(axis=0)
-    ref = m > thr
-    near = np.abs(m - thr) < BAND
+    hot = np.arange(F) < n_hot
+    ref = (m > thr) | hot
+    near = (np.abs(m - thr) < BAND) & ~hot
     got = np.zeros(F, dtype=bool)
     got[got_idx] = True
     bad = (got != ref) & ~near

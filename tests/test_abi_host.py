@@ -164,3 +164,30 @@ def test_workspace_init_rejects_bad_arguments():
     assert lib.psffn_workspace_init(None, 1024, None) == WORKSPACE
     assert lib.psffn_workspace_init(A16 + 16, 1024, None) == WORKSPACE
     assert lib.psffn_workspace_init(A16, 1000, None) == WORKSPACE
+
+
+def test_hot_prefix_calls_reject_bad_prefix():
+    P, W = pred(F=1024), ffn(F=1024)
+    for n_hot in (-1, 1025):
+        assert lib.psffn_predict_hot(B(P), n_hot, fake(), 1, 0.0, fake(), fake(), None, fake(), 1 << 30,
+                                     None) == INVALID
+        assert lib.psffn_layer_hot(B(P), B(W), n_hot, fake(), 1, 0.0, fake(), fake(), None, fake(), 0, fake(),
+                                   1 << 34, None) == INVALID
+    # the remaining checks are those of psffn_predict / psffn_layer
+    assert lib.psffn_predict_hot(B(pred(d=260)), 4, fake(), 1, 0.0, fake(), fake(), None, fake(), 1 << 30,
+                                 None) == UNSUPPORTED
+    assert lib.psffn_layer_hot(B(P), B(W), 4, fake(), 0, 0.0, fake(), fake(), None, fake(), 0, fake(), 1 << 34,
+                               None) == INVALID
+
+
+def test_hot_prefix_len_from_profile_counts():
+    import torch
+    counts = torch.tensor([512, 512, 511, 507, 506, 300, 2, 0], dtype=torch.int32)
+    assert ps.hot_prefix_len(counts, 512, 0.99) == 4  # ceil(0.99 * 512) = 507
+    assert ps.hot_prefix_len(counts, 512, 1.0) == 2
+    assert ps.hot_prefix_len(counts, 512, 0.001) == 7
+    assert ps.hot_prefix_len(torch.zeros(5, dtype=torch.int32), 512, 0.5) == 0
+    with pytest.raises(ValueError):
+        ps.hot_prefix_len(torch.tensor([1, 9], dtype=torch.int32), 10, 0.5)  # not hot-first
+    with pytest.raises(ValueError):
+        ps.hot_prefix_len(counts, 512, 0.0)

@@ -319,3 +319,33 @@ def test_layer_graph_replay_matches_eager(label, B):
         assert torch.equal(y, y_ref), "replay %d differs" % rep
         ps.layer(c["P"], c["W"], x, c["ws"])  # eager work between replays on the same workspace
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("label", [c[0] for c in CASES])
+@pytest.mark.parametrize("B", [1, 3, 8, 32])
+def test_hot_prefix_predict_and_layer(label, B):
+    # neurons [0, n_hot) are listed without prediction; the tail follows the predictor exactly as
+    # in psffn_predict (same logits), and the layer call's y is the sparse FFN on that list
+    c = setup_case(label)
+    x = c["X"][:B].contiguous()
+    F = c["spec"].F
+    ref = oracle.predict_logits(c["n"]["A"], c["n"]["Q"], c["n"]["c"], c["Xn"][:B])
+    logits0 = torch.empty(B, F, device=DEV)
+    ps.predict(c["P"], x, c["ws"], logits=logits0)
+    for n_hot in (1, 37, (F // 3) | 5, F - 3, F):
+        say("hot prefix", label, "B", B, "n_hot", n_hot)
+        logits = torch.empty(B, F, device=DEV)
+        idx, cnt = ps.predict(c["P"], x, c["ws"], logits=logits, n_hot=n_hot)
+        torch.cuda.synchronize()
+        st = check_set(idx, cnt, ref, n_hot=n_hot)
+        assert torch.equal(logits[:, n_hot:], logits0[:, n_hot:])
+        n = int(cnt.item())
+        assert n >= n_hot and torch.equal(idx[:n_hot].cpu(), torch.arange(n_hot, dtype=torch.int32))
+        idx2, cnt2, y2 = ps.layer(c["P"], c["W"], x, c["ws"], n_hot=n_hot)
+        y1 = ps.sparse_ffn(c["W"], x, idx, cnt, c["ws"])
+        torch.cuda.synchronize()
+        assert int(cnt2.item()) == n and torch.equal(idx2[:n], idx[:n])
+        assert torch.equal(y1, y2)
+        if st["exact"]:
+            check_y(y2.cpu().numpy(), c["orc"].sparse_ffn(c["Xn"][:B], oracle.compact(ref, n_hot=n_hot)),
+                    tol_for(c["spec"].storage))
