@@ -69,7 +69,7 @@ CONFIGS = {
 }
 
 _TAGS = {"w_up": 1, "w_gate": 2, "w_dT": 3, "A": 4, "Q": 5, "rank": 6, "tokens": 7, "profile": 8, "density": 9,
-         "x0": 10}
+         "x0": 10, "aligned": 11}
 
 
 def _gen(seed: int, layer: int, tag: str, device) -> torch.Generator:
@@ -226,6 +226,36 @@ def make_layer(spec: LayerSpec, seed: int = 0, layer: int = 0, device="cpu", d: 
     return Layer(spec=spec, w_up=L["w_up"], w_dT=L["w_dT"], w_gate=L.get("w_gate"), s_up=L.get("s_up"),
                  s_gate=L.get("s_gate"), s_dT=L.get("s_dT"), b_up=L.get("b_up"), b_gate=L.get("b_gate"), A=A, Q=Q,
                  c=c, p=p)
+
+
+def make_aligned_predictor(L: Layer, r: int, seed: int = 0):
+    """A predictor ALIGNED with the layer (input construction for the predictor-accuracy study).
+
+    The layer's deciding branch W (W_up for ReLU, W_gate for SwiGLU; dense storage only) is
+    approximated at rank r, W ~= U_r S_r V_r^T, by a seeded randomized range finder with two power
+    iterations; the predictor is A = V_r^T [r][d], Q = U_r S_r [F][r] and c = the branch's bias,
+    stored in the predictor's type, so l = Q (A x) + c approximates the true pre-activation.  The
+    generated predictor of make_layer is instead independent of W (equal firing rates only).
+    Returns (A, Q, c) on the layer's device."""
+    if L.spec.storage == "i4":
+        raise ValueError("make_aligned_predictor: dense layers only")
+    W = (L.w_gate if L.spec.act == "swiglu" else L.w_up).to(torch.float32)
+    bias = L.b_gate if L.spec.act == "swiglu" else L.b_up
+    F, d = W.shape
+    q = min(r + 16, d, F)
+    g = _gen(seed, r, "aligned", W.device)
+    Y = W @ torch.randn(d, q, generator=g, device=W.device, dtype=torch.float32)
+    for _ in range(2):
+        Y, _ = torch.linalg.qr(Y)
+        Y = W @ (W.T @ Y)
+    Qb, _ = torch.linalg.qr(Y)  # F x q orthonormal basis of W's dominant range
+    U_s, S, Vh = torch.linalg.svd(Qb.T @ W, full_matrices=False)  # (q x d) = U_s S Vh
+    U = Qb @ U_s[:, :r]
+    pstore = "f32" if L.spec.storage == "f32" else "f16"
+    A = _store(Vh[:r].contiguous(), pstore).contiguous()
+    Qm = _store((U * S[:r]).contiguous(), pstore).contiguous()
+    c = (bias if bias is not None else torch.zeros(F, device=W.device)).to(torch.float32).contiguous()
+    return A, Qm, c
 
 
 def make_tokens(spec: LayerSpec, n: int, seed: int = 0, stream: str = "tokens", device="cpu", d: int = None):
