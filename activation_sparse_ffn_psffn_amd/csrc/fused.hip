@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
             w[r][j] = dw[r][j];
             sc[r][j] = dsc[r][j];
           }
-        load_down(j0, r0 + RBD);  // the next batch (past the list: the zero block)
+        if (r0 + RBD < nr) load_down(j0, r0 + RBD);  // the next batch, if there is one
 #pragma unroll
         for (int p = 0; p < RBD / 2; ++p) {
           const int r = r0 + 2 * p;
@@ -867,7 +867,7 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
         for (int r = 0; r < RB; ++r)
 #pragma unroll
           for (int u = 0; u < UG; ++u) w[r][u] = dw[r][u];
-        load_down(j0, r0 + RB);  // (past the list: the zero block)
+        if (r0 + RB < nr) load_down(j0, r0 + RB);  // the next batch, if there is one
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
           if (r0 + r >= nr) continue;  // (no break: the loop must unroll, w[r] stays in registers)
