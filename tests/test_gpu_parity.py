@@ -297,12 +297,13 @@ def test_layer_call_equals_two_calls_and_oracle(label, B):
     assert torch.equal(acc, (base + y1) + y1)
 
 
-@pytest.mark.parametrize("label,B", [("f16_relu", 1), ("f16_relu", 8), ("i4_swiglu", 24)])
-def test_layer_graph_replay_matches_eager(label, B):
+@pytest.mark.parametrize("label,B,n_hot", [("f16_relu", 1, 0), ("f16_relu", 8, 0), ("i4_swiglu", 24, 0),
+                                           ("f16_relu", 1, 101), ("f16_swiglu", 3, 700)])
+def test_layer_graph_replay_matches_eager(label, B, n_hot):
     c = setup_case(label)
-    say("graph replay", label, "B", B)
+    say("graph replay", label, "B", B, "n_hot", n_hot)
     x = c["X"][:B].contiguous()
-    idx, cnt, y = ps.layer(c["P"], c["W"], x, c["ws"])
+    idx, cnt, y = ps.layer(c["P"], c["W"], x, c["ws"], n_hot=n_hot)
     y_ref = y.clone()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -310,7 +311,7 @@ def test_layer_graph_replay_matches_eager(label, B):
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            ps.layer(c["P"], c["W"], x, c["ws"], idx=idx, count=cnt, y=y)
+            ps.layer(c["P"], c["W"], x, c["ws"], idx=idx, count=cnt, y=y, n_hot=n_hot)
     torch.cuda.current_stream().wait_stream(s)
     for rep in range(4):
         y.zero_()
