@@ -75,6 +75,29 @@ size_t ffn_need(const psffn_ffn& W, int B) {
   return v;
 }
 
+// Pipeline choice for 2..kFusedMaxBatch tokens, per stage (measured on MI355X at B = 2..4: the
+// MFMA batch pipeline's cost hardly grows with the batch, the small-batch kernels' per-token work
+// does).  Each stage's choice depends on its own descriptor and B only, so that psffn_layer gives
+// exactly the outputs of psffn_predict followed by psffn_sparse_ffn.
+//  * predictor: the batch pipeline from 3 tokens, and at 2 tokens above 1024 ranks (the
+//    small-batch logits kernel then holds three slices of h per token and lane);
+//  * FFN: the batch pipeline for 4-bit weights from 2 tokens and for fp16 ReLU weights from 3;
+//    fp16 SwiGLU layers (about half the neurons active, so the FFN dominates) stream their rows
+//    faster through the small-batch kernel.
+// Above kFusedMaxBatch tokens only the batch pipeline exists.
+bool pred_on_batch(const psffn_predictor& P, int B) {
+  if (B > kFusedMaxBatch) return true;
+  if (!batch_supported_pred(P, B)) return false;
+  return B >= 3 || P.r > 1024;
+}
+
+bool ffn_on_batch(const psffn_ffn& W, int B) {
+  if (B > kFusedMaxBatch) return true;
+  if (!batch_supported_ffn(W, B)) return false;
+  if (W.dt == PSFFN_I4G128) return true;
+  return W.act == PSFFN_RELU && B >= 3;
+}
+
 psffn_status check_ws(const void* ws, size_t ws_bytes, int F, size_t need) {
   if (!ws || !aligned(ws, 256) || ws_bytes < state_layout(F).scratch + need) return PSFFN_E_WORKSPACE;
   return PSFFN_OK;
@@ -143,10 +166,10 @@ psffn_status psffn_predict_hot(const psffn_predictor* P, int n_hot, const void* 
   if (st != PSFFN_OK) return st;
   const St pt = st_of(P->dt);
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch)
-    e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream, n_hot);
-  else
+  if (pred_on_batch(*P, B))
     e = launch_predict_batch(*P, x, B, logit_thr, idx, count, logits, ws, stream, n_hot);
+  if (e == hipErrorNotSupported && B <= kFusedMaxBatch)
+    e = launch_predict_fused(pt, *P, x, B, logit_thr, idx, count, logits, ws, stream, n_hot);
   if (e == hipErrorNotSupported) {
     char* base = static_cast<char*>(ws) + state_layout(P->F).scratch;
     float* h = reinterpret_cast<float*>(base);
@@ -182,10 +205,9 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
   if (st != PSFFN_OK) return st;
   const St wt = st_of(W->dt);
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch)
+  if (ffn_on_batch(*W, B)) e = launch_ffn_batch(*W, x, B, idx, count, y, accumulate, ws, stream);
+  if (e == hipErrorNotSupported && B <= kFusedMaxBatch)
     e = launch_ffn_fused(wt, *W, x, B, idx, count, y, accumulate, ws, stream);
-  else
-    e = launch_ffn_batch(*W, x, B, idx, count, y, accumulate, ws, stream);
   if (e == hipErrorNotSupported) {
     char* base = static_cast<char*>(ws) + state_layout(W->F).scratch;
     float* a = reinterpret_cast<float*>(base);
@@ -221,12 +243,20 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
   st = check_ws(ws, ws_bytes, W->F, need);
   if (st != PSFFN_OK) return st;
   hipError_t e = hipErrorNotSupported;
-  if (B <= kFusedMaxBatch)
-    e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
-  else
+  const bool pb = pred_on_batch(*P, B), fb = ffn_on_batch(*W, B);
+  if (pb && fb) {
     e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
+  } else if (!pb && !fb) {
+    e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
+  } else if (pb) {
+    // batch predictor up to its mask words, then the small-batch FFN orders the list from them (the
+    // list the batch predictor's own list kernel would write, so the outputs equal the two calls)
+    e = launch_predict_batch_masks(*P, x, B, logit_thr, logits, ws, stream);
+    if (e == hipSuccess)
+      e = launch_ffn_fused_scan(st_of(W->dt), *W, x, B, idx, count, y, accumulate, ws, stream, n_hot);
+  }
   if (e != hipErrorNotSupported) return hip_status(e);
-  // shapes outside the one-call path: the two calls, same results
+  // shapes outside the one-call paths: the two calls, same results
   st = psffn_predict_hot(P, n_hot, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
   if (st != PSFFN_OK) return st;
   return psffn_sparse_ffn(W, x, B, idx, count, y, accumulate, ws, ws_bytes, stream);

@@ -1158,12 +1158,12 @@ size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_ac
 }
 
 bool batch_supported_pred(const psffn_predictor& P, int B) {
-  return B > kFusedMaxBatch && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF &&
+  return B >= 2 && B <= 32 && P.dt == PSFFN_F16 && P.F <= kBatchMaxF &&
          (size_t)P.r * P.d * 2 <= kMaxBufferBytes;  // k_bh reads A through one buffer resource
 }
 bool batch_supported_ffn(const psffn_ffn& W, int B) {
   const size_t rowb = W.dt == PSFFN_I4G128 ? (size_t)W.d / 2 : (size_t)W.d * 2;
-  return B > kFusedMaxBatch && B <= 32 && (W.dt == PSFFN_F16 || W.dt == PSFFN_I4G128) && W.F <= kBatchMaxF &&
+  return B >= 2 && B <= 32 && (W.dt == PSFFN_F16 || W.dt == PSFFN_I4G128) && W.F <= kBatchMaxF &&
          (size_t)W.F * rowb <= kMaxBufferBytes;
 }
 
@@ -1336,6 +1336,15 @@ static hipError_t predict_and_scan(const BArgs& g, hipStream_t s) {
   if (e != hipSuccess) return e;
   k_bscan<<<1, kScanThreads, 8 * (size_t)g.nq + 4, s>>>(g);
   return hipSuccess;
+}
+
+hipError_t launch_predict_batch_masks(const psffn_predictor& P, const void* x, int B, float thr, float* logits,
+                                      void* ws, hipStream_t s) {
+  if (!batch_supported_pred(P, B)) return hipErrorNotSupported;
+  BArgs g{};
+  pred_args(g, P, x, B, thr, logits, ws);
+  const hipError_t e = g.B <= 16 ? pred_launch<1>(g, s) : pred_launch<2>(g, s);
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,

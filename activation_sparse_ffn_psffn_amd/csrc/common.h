@@ -161,17 +161,25 @@ hipError_t launch_predict_fused(St st, const psffn_predictor& P, const void* x, 
                                 int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot = 0);
 hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
                             float* y, int accumulate, void* ws, hipStream_t s);
+// the small-batch FFN from the mask words of a predictor call in the same workspace (the list and its
+// length are ordered inside the fused kernel and written to idx/count, as in launch_layer_fused)
+hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count,
+                                 float* y, int accumulate, void* ws, hipStream_t s, int n_hot);
 hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
                               hipStream_t s, int n_hot = 0);
 
-// batch pipeline (kFusedMaxBatch < B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA
-// tiles; the same NotSupported convention
+// batch pipeline (2 <= B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA tiles; the
+// same NotSupported convention.  Above kFusedMaxBatch tokens it is the only pipeline; from 2 to
+// kFusedMaxBatch tokens the calls choose per stage (pred_on_batch / ffn_on_batch in api.hip).
 bool batch_supported_pred(const psffn_predictor& P, int B);
 bool batch_supported_ffn(const psffn_ffn& W, int B);
 size_t batch_scratch_bytes(int B, int d, int r, int F, psffn_dtype wdt, psffn_act act, bool pred, bool ffn);
 hipError_t launch_predict_batch(const psffn_predictor& P, const void* x, int B, float thr, int32_t* idx,
                                 int32_t* count, float* logits, void* ws, hipStream_t s, int n_hot = 0);
+// the batch predictor's kernels up to its mask words (in the workspace's mask region), no list
+hipError_t launch_predict_batch_masks(const psffn_predictor& P, const void* x, int B, float thr, float* logits,
+                                      void* ws, hipStream_t s);
 hipError_t launch_ffn_batch(const psffn_ffn& W, const void* x, int B, const int32_t* idx, const int32_t* count,
                             float* y, int accumulate, void* ws, hipStream_t s);
 hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,

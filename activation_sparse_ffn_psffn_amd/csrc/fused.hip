@@ -162,22 +162,25 @@ __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const 
       const int i = i0 + k, e = v * kWave * EPL + lane * EPL;
       qv[k][v] = ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && i >= n_hot && e < r);
     }
+  // h (all tokens, fp32, zero past r) goes through LDS once per workgroup: the four waves share it
+  constexpr int HR = RV * kWave * EPL;  // h elements per token covered by the lanes' slices
+  __shared__ float4 s_h[NB * HR / 4];
+  for (int k = threadIdx.x; k < NB * HR / 4; k += kBlock) {
+    const int b = k / (HR / 4), e = (k % (HR / 4)) * 4;  // r % 8 == 0: whole float4s
+    s_h[k] = b < nb && e < r ? *reinterpret_cast<const float4*>(h + (size_t)b * r + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
   float hv[NB][RV][EPL];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int v = 0; v < RV; ++v) {
       const int e = v * kWave * EPL + lane * EPL;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) hv[b][v][k] = 0.f;
-      if (b < nb && e < r) {
-        const float* hp = h + (size_t)b * r + e;
-        const float4 a0 = *reinterpret_cast<const float4*>(hp);
-        hv[b][v][0] = a0.x; hv[b][v][1] = a0.y; hv[b][v][2] = a0.z; hv[b][v][3] = a0.w;
-        if constexpr (EPL == 8) {
-          const float4 a1 = *reinterpret_cast<const float4*>(hp + 4);
-          hv[b][v][4] = a1.x; hv[b][v][5] = a1.y; hv[b][v][6] = a1.z; hv[b][v][7] = a1.w;
-        }
+      const float4 a0 = s_h[(b * HR + e) / 4];
+      hv[b][v][0] = a0.x; hv[b][v][1] = a0.y; hv[b][v][2] = a0.z; hv[b][v][3] = a0.w;
+      if constexpr (EPL == 8) {
+        const float4 a1 = s_h[(b * HR + e) / 4 + 1];
+        hv[b][v][4] = a1.x; hv[b][v][5] = a1.y; hv[b][v][6] = a1.z; hv[b][v][7] = a1.w;
       }
     }
   uint32_t mask = 0;
@@ -292,6 +295,7 @@ struct FfnArgs {
   float* part;
   float* y;
   int B, d, F, accumulate;
+  int n_hot;  // layer path: neurons [0, n_hot) are listed whatever the mask words say
 };
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.f + expf(-g)); }
@@ -485,6 +489,12 @@ __global__ __launch_bounds__(kBlock) void k_ud(FfnArgs g) {
         if (q < g.nq) s_mask[q] = mv[u];
       }
       for (int q = threadIdx.x + MW * kBlock; q < g.nq; q += kBlock) s_mask[q] = g.masks[q];
+      // the hot prefix's bits (n_hot <= F: no bit past F is set)
+      const int nwh = (g.n_hot + 31) / 32;
+      for (int q = threadIdx.x; q < nwh; q += kBlock) {
+        const int nh = g.n_hot - 32 * q;
+        s_mask[q] |= nh >= 32 ? 0xffffffffu : (1u << nh) - 1u;
+      }
     }
     __syncthreads();
   }
@@ -1104,8 +1114,47 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
   return ffn_nb<St::I4, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s);
 }
 
-// ---- one decode step of one layer: k_h, k_q (mask words only), k_ud (orders the list from the
+// ---- the FFN from mask words already in the workspace: k_ud in scan mode (orders the list from the
 // masks, writes idx/count, the activations and the down-projection partials), k_reduce_ud
+
+template <St WT, psffn_act ACT, int NB>
+static hipError_t ffn_scan_t(const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count, float* y,
+                             int accumulate, void* ws, hipStream_t s, int n_hot) {
+  const int NQ = (W.F + 31) / 32;
+  const size_t ud = round256((size_t)B * W.d * (WT == St::F32 ? 4 : 2)) + round256(4 * (size_t)(2 * NQ + 1)) +
+                    4 * (size_t)kUDMaxRows * NB + 4 * (size_t)kUDMaxRows;
+  if (!ffn_fits<WT>(W, B) || NQ > kMaxScanChunks || ud > (size_t)150 * 1024) return hipErrorNotSupported;
+  FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
+  g.masks = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + state_layout(W.F).masks);
+  g.nq = NQ;
+  g.idx_out = idx;
+  g.count_out = count;
+  g.n_hot = n_hot;
+  return ffn_launch<WT, ACT, NB, true>(g, s);
+}
+
+template <St WT, psffn_act ACT>
+static hipError_t ffn_scan_nb(const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count, float* y,
+                              int accumulate, void* ws, hipStream_t s, int n_hot) {
+  if (B == 1) return ffn_scan_t<WT, ACT, 1>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  if (B == 2) return ffn_scan_t<WT, ACT, 2>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  if (B <= 4) return ffn_scan_t<WT, ACT, 4>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  return hipErrorNotSupported;
+}
+
+hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count,
+                                 float* y, int accumulate, void* ws, hipStream_t s, int n_hot) {
+  if (W.act == PSFFN_RELU) {
+    if (st == St::F32) return ffn_scan_nb<St::F32, PSFFN_RELU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+    if (st == St::F16) return ffn_scan_nb<St::F16, PSFFN_RELU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+    return ffn_scan_nb<St::I4, PSFFN_RELU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  }
+  if (st == St::F32) return ffn_scan_nb<St::F32, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  if (st == St::F16) return ffn_scan_nb<St::F16, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  return ffn_scan_nb<St::I4, PSFFN_SWIGLU>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+}
+
+// ---- one decode step of one layer: k_h, k_q (mask words only), then the FFN from the mask words
 
 template <St PT, St WT, psffn_act ACT, int NB, int RV>
 static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
@@ -1127,12 +1176,7 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
-  FfnArgs g = ffn_args<WT>(W, x, B, idx, count, y, accumulate, ws);
-  g.masks = masks;
-  g.nq = NQ;
-  g.idx_out = idx;
-  g.count_out = count;
-  return ffn_launch<WT, ACT, NB, true>(g, s);
+  return ffn_scan_t<WT, ACT, NB>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
 }
 
 template <St PT, St WT, psffn_act ACT, int NB>

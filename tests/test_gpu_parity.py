@@ -55,7 +55,7 @@ def say(*a):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [1, 3, 8, 32])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 32])
 def test_predict_sets_and_logits(label, B):
     c = setup_case(label)
     say("predict", label, "B", B)
@@ -72,7 +72,7 @@ def test_predict_sets_and_logits(label, B):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [1, 2, 8, 32])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 32])
 def test_sparse_ffn_on_oracle_list(label, B):
     c = setup_case(label)
     say("sparse_ffn", label, "B", B)
@@ -268,7 +268,7 @@ def test_layernorm_f16(B, d):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [1, 3, 8, 20, 32])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8, 20, 32])
 def test_layer_call_equals_two_calls_and_oracle(label, B):
     c = setup_case(label)
     say("layer", label, "B", B)
@@ -323,7 +323,7 @@ def test_layer_graph_replay_matches_eager(label, B, n_hot):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [1, 3, 8, 32])
+@pytest.mark.parametrize("B", [1, 2, 4, 8, 32])
 def test_hot_prefix_predict_and_layer(label, B):
     # neurons [0, n_hot) are listed without prediction; the tail follows the predictor exactly as
     # in psffn_predict (same logits), and the layer call's y is the sparse FFN on that list
