@@ -63,6 +63,8 @@ _lib.psffn_predict_hot.restype = _i
 _lib.psffn_predict_hot.argtypes = [_P(_Predictor), _i, _vp, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.psffn_layer_hot.restype = _i
 _lib.psffn_layer_hot.argtypes = [_P(_Predictor), _P(_FFN), _i, _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
+_lib.psffn_layer_ln.restype = _i
+_lib.psffn_layer_ln.argtypes = [_P(_Predictor), _P(_FFN), _vp, _f, _vp, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.psffn_profile_counts.restype = _i
 _lib.psffn_profile_counts.argtypes = [_P(_FFN), _vp, _i, _vp, _vp]
 _lib.psffn_permute_hot_first.restype = _i
@@ -72,7 +74,8 @@ _lib.psffn_layernorm_f16.restype = _i
 _lib.psffn_layernorm_f16.argtypes = [_vp, _i, _i, _f, _vp, _vp]
 
 EXPORTED = ("psffn_status_str", "psffn_workspace_bytes", "psffn_workspace_init", "psffn_predict", "psffn_compact",
-            "psffn_sparse_ffn", "psffn_layer", "psffn_predict_hot", "psffn_layer_hot", "psffn_profile_counts",
+            "psffn_sparse_ffn", "psffn_layer", "psffn_predict_hot", "psffn_layer_hot", "psffn_layer_ln",
+            "psffn_profile_counts",
             "psffn_permute_hot_first",
             "psffn_layernorm_f16")
 
@@ -242,6 +245,26 @@ def layer(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, thr: float = 
                             _ptr(logits), _ptr(y), int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream)),
            "layer")
     return idx, count, y
+
+
+def layer_ln(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, eps: float = 1e-5, h: torch.Tensor = None,
+             thr: float = 0.0, idx: torch.Tensor = None, count: torch.Tensor = None, logits: torch.Tensor = None,
+             stream=None):
+    """One decode-stack step on the fp32 residual x [B][d], in place: h = fp16(LayerNorm(x)), then
+    x += the sparse FFN of h (psffn_layer_ln).  Returns (idx, count, h)."""
+    B, d = x.shape
+    F = P.Q.shape[0]
+    if idx is None:
+        idx = torch.empty(F, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if h is None:
+        h = torch.empty(B, d, dtype=torch.float16, device=x.device)
+    sp, sw = P.struct(), W.struct()
+    _check(_lib.psffn_layer_ln(ctypes.byref(sp), ctypes.byref(sw), _ptr(x), float(eps), _ptr(h), B, float(thr),
+                               _ptr(idx), _ptr(count), _ptr(logits), _ptr(ws), ws.numel(), _stream(stream)),
+           "layer_ln")
+    return idx, count, h
 
 
 def profile_counts(W: FFN, X: torch.Tensor, counts: torch.Tensor = None, stream=None) -> torch.Tensor:

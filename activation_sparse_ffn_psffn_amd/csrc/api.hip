@@ -262,6 +262,39 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
   return psffn_sparse_ffn(W, x, B, idx, count, y, accumulate, ws, ws_bytes, stream);
 }
 
+psffn_status psffn_layer_ln(const psffn_predictor* P, const psffn_ffn* W, float* x, float eps, void* h, int B,
+                            float logit_thr, int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  psffn_status st = check_pred(P);
+  if (st == PSFFN_OK) st = check_ffn(W);
+  if (st != PSFFN_OK) return st;
+  if (P->F != W->F || P->d != W->d) return PSFFN_E_INVALID_ARG;
+  if (P->dt != PSFFN_F16) return PSFFN_E_UNSUPPORTED;  // the LayerNorm output (the FFN input) is fp16
+  const int d = P->d;
+  if (!batch_ok(B) || !x || !aligned(x, 16) || !h || !aligned(h, 16) || !idx || !aligned(idx, 4) || !count ||
+      !aligned(count, 4) || (logits && !aligned(logits, 4)) || logit_thr != logit_thr || !(eps >= 0.f) ||
+      overlaps(x, (size_t)B * d * 4, h, (size_t)B * d * 2))
+    return PSFFN_E_INVALID_ARG;
+  size_t need = pred_need(*P, B);
+  const size_t f = ffn_need(*W, B);
+  need = f > need ? f : need;
+  st = check_ws(ws, ws_bytes, W->F, need);
+  if (st != PSFFN_OK) return st;
+  hipError_t e = hipErrorNotSupported;
+  if (B <= kFusedMaxBatch && !pred_on_batch(*P, B) && !ffn_on_batch(*W, B)) {
+    LnArgs ln;
+    ln.xres = x;
+    ln.eps = eps;
+    ln.hout = static_cast<_Float16*>(h);
+    e = launch_layer_fused(*P, *W, h, B, logit_thr, idx, count, logits, x, 1, ws, stream, 0, ln);
+  }
+  if (e != hipErrorNotSupported) return hip_status(e);
+  // the other pipelines: the LayerNorm kernel, then the layer call (the same results)
+  e = launch_layernorm_f16(x, B, d, eps, h, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return psffn_layer(P, W, h, B, logit_thr, idx, count, logits, x, 1, ws, ws_bytes, stream);
+}
+
 psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int32_t* counts, hipStream_t stream) {
   psffn_status st = check_ffn(W);
   if (st != PSFFN_OK) return st;

@@ -130,6 +130,67 @@ __host__ __device__ inline StateLayout state_layout(int F) {
   return s;
 }
 
+// Sum over a workgroup of kBlock threads (wave sums, then the wave totals in wave order).
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (wave_lane() == 0) s_red[wave_id()] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int k = 0; k < kBlock / kWave; ++k) t += s_red[k];
+  return t;
+}
+
+// One LayerNorm row (gamma 1, beta 0, population variance, fp16 result) by a workgroup of kBlock
+// threads, the row held in registers: thread t holds float4 j = t + k kBlock (k < K, d % 4 == 0).
+// Two block reductions (mean, then the centred sum of squares), then out[j] = 4 halves (uint2;
+// global or LDS).  The LayerNorm kernel and the layer call's first kernel both use it, so they give
+// the same bits.
+template <int K>
+__device__ __forceinline__ void ln_row_f16(const float* __restrict__ xrow, int d, float eps, float* s_red,
+                                           uint2* out) {
+  const float4* xr = reinterpret_cast<const float4*>(xrow);
+  const int n4 = d / 4;
+  float4 v[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = threadIdx.x + k * kBlock;
+    v[k] = j < n4 ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float sm = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) sm += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+  const float mean = block_sum(sm, s_red) / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    if (threadIdx.x + k * kBlock < n4) {
+      const float a = v[k].x - mean, b = v[k].y - mean, c = v[k].z - mean, e = v[k].w - mean;
+      q = fmaf(a, a, q);
+      q = fmaf(b, b, q);
+      q = fmaf(c, c, q);
+      q = fmaf(e, e, q);
+    }
+  }
+  const float var = block_sum(q, s_red) / (float)d;
+  const float inv = 1.f / sqrtf(var + eps);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = threadIdx.x + k * kBlock;
+    if (j < n4) {
+      const half2_t lo = {(_Float16)((v[k].x - mean) * inv), (_Float16)((v[k].y - mean) * inv)};
+      const half2_t hi = {(_Float16)((v[k].z - mean) * inv), (_Float16)((v[k].w - mean) * inv)};
+      out[j] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    }
+  }
+}
+
+// float4 per thread that ln_row_f16 needs for a row of d (1, 2, 4, 8 or 16; 0 above 16384)
+inline int ln_k(int d) {
+  const int k = (d / 4 + kBlock - 1) / kBlock;
+  return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : k <= 16 ? 16 : 0;
+}
+
 // ----------------------------------------------------------------------------------------
 // launchers (return hipSuccess or the launch error)
 
@@ -165,9 +226,16 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
 // length are ordered inside the fused kernel and written to idx/count, as in launch_layer_fused)
 hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count,
                                  float* y, int accumulate, void* ws, hipStream_t s, int n_hot);
+// LayerNorm folded into the layer call (stack step): xres = the fp32 residual (the input of the
+// LayerNorm), hout = its fp16 LayerNorm output, written by the call and read by its FFN
+struct LnArgs {
+  const float* xres = nullptr;
+  float eps = 0.f;
+  _Float16* hout = nullptr;
+};
 hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s, int n_hot = 0);
+                              hipStream_t s, int n_hot = 0, const LnArgs& ln = LnArgs{});
 
 // batch pipeline (2 <= B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA tiles; the
 // same NotSupported convention.  Above kFusedMaxBatch tokens it is the only pipeline; from 2 to

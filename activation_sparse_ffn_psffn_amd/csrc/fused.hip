@@ -68,9 +68,12 @@ __device__ __forceinline__ void stage_x(const void* __restrict__ x, size_t n, ui
 // (Two-wave workgroups, twice as many, measured 0.4 µs slower on a 1024 x 7168 fp16 A.)
 constexpr int kHThreads = 256;
 
-template <St PT, int NB>
+// LNK > 0 (fp16 predictor, stack step): x is the fp32 residual [nb][d]; every workgroup normalises
+// it into LDS with ln_row_f16<LNK> (the LayerNorm kernel's arithmetic), and workgroup 0 also
+// stores the fp16 rows to hout for the FFN kernel.
+template <St PT, int NB, int LNK>
 __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, const void* __restrict__ x, int d, int r,
-                                              int nb, float* __restrict__ h) {
+                                              int nb, float* __restrict__ h, float eps, _Float16* __restrict__ hout) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int UN = 16;
@@ -86,7 +89,20 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
     const int e = base + u * kWave * EPL;
     w[u] = ld16z(arow + (size_t)e * ESZ, j < r && e < d);
   }
-  stage_x<kHThreads>(x, (size_t)nb * d * ESZ, s_x);
+  if constexpr (LNK > 0) {
+    static_assert(PT == St::F16, "the LayerNorm output is fp16");
+    __shared__ float s_red[kHThreads / kWave];
+    for (int b = 0; b < nb; ++b)
+      ln_row_f16<LNK>(reinterpret_cast<const float*>(x) + (size_t)b * d, d, eps, s_red,
+                      reinterpret_cast<uint2*>(s_x) + (size_t)b * d / 4);
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      const int n16 = nb * d / 8;  // d % 8 == 0
+      for (int k = threadIdx.x; k < n16; k += kHThreads) reinterpret_cast<uint4*>(hout)[k] = s_x[k];
+    }
+  } else {
+    stage_x<kHThreads>(x, (size_t)nb * d * ESZ, s_x);
+  }
   if (j >= r) return;
   const char* xs = reinterpret_cast<const char*>(s_x);
   float acc[NB];
@@ -990,7 +1006,8 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  k_h<PT, NB, 0><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h,
+                                                                                             0.f, nullptr);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
   k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
   return hipGetLastError();
@@ -1159,7 +1176,10 @@ hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B
 template <St PT, St WT, psffn_act ACT, int NB, int RV>
 static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
                           int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
-                          int n_hot) {
+                          int n_hot, const LnArgs& ln) {
+  const float* xres = ln.xres;
+  const float eps = ln.eps;
+  _Float16* hout = ln.hout;
   constexpr int RPW = 4;                  // k_q chunks of 16 neurons (32 KB of Q rows in flight each)
   const int NQ = (P.F + 31) / 32;         // 32-bit mask words
   const int NC = (P.F + 4 * RPW - 1) / (4 * RPW);
@@ -1174,52 +1194,69 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h);
+  const int hgrid = (P.r + kHThreads / kWave - 1) / (kHThreads / kWave);
+  if (xres == nullptr) {
+    k_h<PT, NB, 0><<<hgrid, kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h, 0.f, nullptr);
+  } else {
+    if constexpr (PT != St::F16) return hipErrorNotSupported;
+    else {
+      const int k = ln_k(P.d);
+      if (k == 1) k_h<PT, NB, 1><<<hgrid, kHThreads, xbytes, s>>>(P.A, xres, P.d, P.r, B, h, eps, hout);
+      else if (k == 2) k_h<PT, NB, 2><<<hgrid, kHThreads, xbytes, s>>>(P.A, xres, P.d, P.r, B, h, eps, hout);
+      else if (k == 4) k_h<PT, NB, 4><<<hgrid, kHThreads, xbytes, s>>>(P.A, xres, P.d, P.r, B, h, eps, hout);
+      else if (k == 8) k_h<PT, NB, 8><<<hgrid, kHThreads, xbytes, s>>>(P.A, xres, P.d, P.r, B, h, eps, hout);
+      else if (k == 16) k_h<PT, NB, 16><<<hgrid, kHThreads, xbytes, s>>>(P.A, xres, P.d, P.r, B, h, eps, hout);
+      else return hipErrorNotSupported;
+    }
+  }
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
-  return ffn_scan_t<WT, ACT, NB>(W, x, B, idx, count, y, accumulate, ws, s, n_hot);
+  return ffn_scan_t<WT, ACT, NB>(W, xres ? static_cast<const void*>(hout) : x, B, idx, count, y, accumulate, ws, s,
+                                 n_hot);
 }
 
 template <St PT, St WT, psffn_act ACT, int NB>
 static hipError_t layer_rv(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
                            int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
-                           int n_hot) {
+                           int n_hot, const LnArgs& ln) {
   const int per = kWave * Tr<PT>::EPL;
   const int rv = (P.r + per - 1) / per;
-  if (rv == 1) return layer_t<PT, WT, ACT, NB, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  if (rv == 2) return layer_t<PT, WT, ACT, NB, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  if (rv == 3) return layer_t<PT, WT, ACT, NB, 3>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  if (rv == 4) return layer_t<PT, WT, ACT, NB, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+  if (rv == 1) return layer_t<PT, WT, ACT, NB, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  if (rv == 2) return layer_t<PT, WT, ACT, NB, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  if (rv == 3) return layer_t<PT, WT, ACT, NB, 3>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  if (rv == 4) return layer_t<PT, WT, ACT, NB, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
   return hipErrorNotSupported;
 }
 
 template <St PT, St WT, psffn_act ACT>
 static hipError_t layer_nb(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr, int32_t* idx,
                            int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
-                           int n_hot) {
-  if (B == 1) return layer_rv<PT, WT, ACT, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  if (B == 2) return layer_rv<PT, WT, ACT, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  if (B <= 4) return layer_rv<PT, WT, ACT, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+                           int n_hot, const LnArgs& ln) {
+  if (B == 1) return layer_rv<PT, WT, ACT, 1>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  if (B == 2) return layer_rv<PT, WT, ACT, 2>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  if (B <= 4) return layer_rv<PT, WT, ACT, 4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
   return hipErrorNotSupported;
 }
 
 template <St PT, St WT>
 static hipError_t layer_act(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                             int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                            hipStream_t s, int n_hot) {
+                            hipStream_t s, int n_hot, const LnArgs& ln) {
   if (W.act == PSFFN_RELU)
-    return layer_nb<PT, WT, PSFFN_RELU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
-  return layer_nb<PT, WT, PSFFN_SWIGLU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+    return layer_nb<PT, WT, PSFFN_RELU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  return layer_nb<PT, WT, PSFFN_SWIGLU>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
 }
 
 hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, const void* x, int B, float thr,
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
-                              hipStream_t s, int n_hot) {
-  if (P.dt == PSFFN_F32 && W.dt == PSFFN_F32)
-    return layer_act<St::F32, St::F32>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+                              hipStream_t s, int n_hot, const LnArgs& ln) {
+  if (P.dt == PSFFN_F32 && W.dt == PSFFN_F32) {
+    if (ln.xres) return hipErrorNotSupported;
+    return layer_act<St::F32, St::F32>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
+  }
   if (P.dt == PSFFN_F16 && W.dt == PSFFN_F16)
-    return layer_act<St::F16, St::F16>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+    return layer_act<St::F16, St::F16>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
   if (P.dt == PSFFN_F16 && W.dt == PSFFN_I4G128)
-    return layer_act<St::F16, St::I4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot);
+    return layer_act<St::F16, St::I4>(P, W, x, B, thr, idx, count, logits, y, accumulate, ws, s, n_hot, ln);
   return hipErrorNotSupported;
 }
 

@@ -74,16 +74,6 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(const U* __restrict__ sr
 
 // out[b] = fp16(LayerNorm(x[b])), gamma 1, beta 0, population variance, two passes (mean, then
 // the mean of squared deviations).  One workgroup per token.
-__device__ __forceinline__ float block_sum(float v, float* s_red) {
-  v = wave_sum(v);
-  __syncthreads();
-  if (wave_lane() == 0) s_red[wave_id()] = v;
-  __syncthreads();
-  float t = 0.f;
-  for (int k = 0; k < kBlock / kWave; ++k) t += s_red[k];
-  return t;
-}
-
 __global__ __launch_bounds__(kBlock) void k_layernorm_f16(const float* __restrict__ x, int d, float eps,
                                                           _Float16* __restrict__ out) {
   __shared__ float s_red[kBlock / kWave];
@@ -109,41 +99,7 @@ template <int K>
 __global__ __launch_bounds__(kBlock) void k_layernorm_f16_reg(const float* __restrict__ x, int d, float eps,
                                                               _Float16* __restrict__ out) {
   __shared__ float s_red[kBlock / kWave];
-  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)blockIdx.x * d);
-  const int n4 = d / 4;
-  float4 v[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int j = threadIdx.x + k * kBlock;
-    v[k] = j < n4 ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  float sm = 0.f;
-#pragma unroll
-  for (int k = 0; k < K; ++k) sm += (v[k].x + v[k].y) + (v[k].z + v[k].w);
-  const float mean = block_sum(sm, s_red) / (float)d;
-  float q = 0.f;
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    if (threadIdx.x + k * kBlock < n4) {
-      const float a = v[k].x - mean, b = v[k].y - mean, c = v[k].z - mean, e = v[k].w - mean;
-      q = fmaf(a, a, q);
-      q = fmaf(b, b, q);
-      q = fmaf(c, c, q);
-      q = fmaf(e, e, q);
-    }
-  }
-  const float var = block_sum(q, s_red) / (float)d;
-  const float inv = 1.f / sqrtf(var + eps);
-  uint2* o = reinterpret_cast<uint2*>(out + (size_t)blockIdx.x * d);
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int j = threadIdx.x + k * kBlock;
-    if (j < n4) {
-      const half2_t lo = {(_Float16)((v[k].x - mean) * inv), (_Float16)((v[k].y - mean) * inv)};
-      const half2_t hi = {(_Float16)((v[k].z - mean) * inv), (_Float16)((v[k].w - mean) * inv)};
-      o[j] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-    }
-  }
+  ln_row_f16<K>(x + (size_t)blockIdx.x * d, d, eps, s_red, reinterpret_cast<uint2*>(out + (size_t)blockIdx.x * d));
 }
 
 __global__ __launch_bounds__(kBlock) void k_fill_zero(uint4* __restrict__ p, size_t n16) {

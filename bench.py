@@ -316,8 +316,8 @@ def bench_stack(args, spec, ps, synth, np, torch):
 
     def step(st):
         for l, (P, W, _) in enumerate(layers):
-            ps.layernorm_f16(x, 1e-5, out=hbuf, stream=st)
-            ps.layer(P, W, hbuf, ws, idx=idx, count=cnts[l:l + 1], y=x, accumulate=True, stream=st)
+            # x <- x + FFN(fp16(LayerNorm(x))) in one library call
+            ps.layer_ln(P, W, x, ws, eps=1e-5, h=hbuf, idx=idx, count=cnts[l:l + 1], stream=st)
 
     for _ in range(max(1, args.warmup // 16)):
         step(stream)

@@ -162,6 +162,19 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
                              float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y, int accumulate,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* One step of a decode stack (the residual update between layers), in one call:
+ *   h = fp16(LayerNorm(x))   (gamma 1, beta 0, population variance, eps; as psffn_layernorm_f16)
+ *   x += FFN restricted to the predicted neurons of h   (psffn_layer on h with y = x, accumulate)
+ * with exactly the outputs of psffn_layernorm_f16 followed by that psffn_layer call.
+ *   x    in/out, fp32 [B][d] residual, 16-byte aligned
+ *   h    out, fp16 [B][d] (16-byte aligned, not overlapping x): the FFN input
+ *   P    fp16 predictor (E_UNSUPPORTED otherwise); the other arguments as psffn_layer.
+ * Where the small-batch pipeline runs the layer, the LayerNorm is computed inside the layer's first
+ * kernel (no separate launch). */
+psffn_status psffn_layer_ln(const psffn_predictor* P, const psffn_ffn* W, float* x, float eps, void* h, int B,
+                            float logit_thr, int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Offline activation profile (Summary, 2nd paragraph: models are profiled offline):
  * counts[i] = number of the T tokens X [T][d] for which neuron i truly fires -- the ReLU
  * pre-activation W_up[i].x + b_up[i] > 0, or for SwiGLU the gate W_gate[i].x + b_gate[i] > 0.

@@ -191,3 +191,17 @@ def test_hot_prefix_len_from_profile_counts():
         ps.hot_prefix_len(torch.tensor([1, 9], dtype=torch.int32), 10, 0.5)  # not hot-first
     with pytest.raises(ValueError):
         ps.hot_prefix_len(counts, 512, 0.0)
+
+
+def test_layer_ln_rejects_bad_arguments():
+    P, W = pred(F=1024), ffn(F=1024)
+    x, h = fake(), fake()
+    call = lambda P=P, x=x, h=h, eps=1e-5, Bn=1: lib.psffn_layer_ln(B(P), B(W), x, eps, h, Bn, 0.0, fake(), fake(),
+                                                                     None, fake(), 1 << 34, None)
+    assert call(P=pred(F=1024, dt=ps.PSFFN_F32)) == UNSUPPORTED
+    assert call(h=x) == INVALID  # the LayerNorm output overlaps the residual
+    assert call(h=x + 256 * 4 - 16) == INVALID  # partial overlap (B = 1, d = 256: the residual is 1 KB)
+    assert call(h=A16 + 8) == INVALID  # misaligned
+    assert call(eps=-1.0) == INVALID
+    assert call(eps=float("nan")) == INVALID
+    assert call(Bn=0) == INVALID

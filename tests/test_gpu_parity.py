@@ -350,3 +350,50 @@ def test_hot_prefix_predict_and_layer(label, B):
         if st["exact"]:
             check_y(y2.cpu().numpy(), c["orc"].sparse_ffn(c["Xn"][:B], oracle.compact(ref, n_hot=n_hot)),
                     tol_for(c["spec"].storage))
+
+
+@pytest.mark.parametrize("label", ["f16_relu", "f16_swiglu", "i4_relu", "i4_swiglu", "f16_relu_wide", "i4_relu_wide"])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+def test_layer_ln_equals_layernorm_then_layer(label, B):
+    # the stack step in one call (LayerNorm folded into the small-batch layer's first kernel) gives
+    # the bits of psffn_layernorm_f16 followed by psffn_layer accumulating into the residual
+    c = setup_case(label)
+    say("layer_ln", label, "B", B)
+    d, F = c["spec"].d, c["spec"].F
+    x0 = synth.make_residual(c["spec"], B, seed=5, device=DEV, d=d).contiguous()
+    x1 = x0.clone()
+    h1 = ps.layernorm_f16(x1)
+    lg1 = torch.empty(B, F, device=DEV)
+    idx1, cnt1, _ = ps.layer(c["P"], c["W"], h1, c["ws"], logits=lg1, y=x1, accumulate=True)
+    x2 = x0.clone()
+    lg2 = torch.empty(B, F, device=DEV)
+    idx2, cnt2, h2 = ps.layer_ln(c["P"], c["W"], x2, c["ws"], logits=lg2)
+    torch.cuda.synchronize()
+    n = int(cnt1.item())
+    assert torch.equal(h1, h2)
+    assert torch.equal(lg1, lg2)
+    assert int(cnt2.item()) == n and torch.equal(idx1[:n], idx2[:n])
+    assert torch.equal(x1, x2)
+    # and through a graph, replayed with eager work in between
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    x3 = x0.clone()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            ps.layer_ln(c["P"], c["W"], x3, c["ws"], h=h2, idx=idx2, count=cnt2, stream=st)
+    torch.cuda.current_stream().wait_stream(st)
+    for rep in range(3):
+        x3.copy_(x0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(x3, x1), "replay %d differs" % rep
+        ps.layer(c["P"], c["W"], h1, c["ws"])
+        torch.cuda.synchronize()
+
+
+def test_layer_ln_needs_an_fp16_predictor():
+    c = setup_case("f32_relu")
+    x = synth.make_residual(c["spec"], 1, seed=5, device=DEV, d=c["spec"].d).contiguous()
+    with pytest.raises(ps.PsffnError):
+        ps.layer_ln(c["P"], c["W"], x, c["ws"])
