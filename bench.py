@@ -36,8 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 # (hash below); after any change to them the traffic is reported as null until measured again.
 TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/fused.hip")
 TRAFFIC = {
-    # (workload, batch): fetch KiB k_h 7263.1 + k_q 28823.1 + k_list 4.5, write KiB 8.0 + 28.0 + 3.4
-    ("opt30b_relu_f16", 1): {"sources": "c521b89afec7c736", "bytes": 73953987},
+    # (workload, batch): fetch KiB k_h 7263.1 + k_q 28831.1 + k_list 4.1, write KiB 8.0 + 28.0 + 3.4
+    ("opt30b_relu_f16", 1): {"sources": "2f36a8a9018b0586", "bytes": 73969683},
 }
 
 
@@ -63,12 +63,13 @@ def log(*a):
 
 def algorithmic_bytes(spec, B, n_active, n_hot=0):
     """Bytes the method must move for one step with n_active listed neurons (per-step mean).
-    With a hot prefix (B <= 4) the predictor reads the Q rows and biases of the other F - n_hot
-    neurons only."""
+    With a hot prefix, the small-batch predictor (fp32 up to 4 tokens; fp16 at 1 token, and at 2
+    up to 1024 ranks) reads the Q rows and biases of the other F - n_hot neurons only."""
     e_p = 4 if spec.storage == "f32" else 2
     e_x = 4 if spec.storage == "f32" else 2
     d, F, r = spec.d, spec.F, spec.r
-    Fq = F - n_hot if B <= 4 else F
+    small = B <= 4 if spec.storage == "f32" else (B == 1 or (B == 2 and r <= 1024))
+    Fq = F - n_hot if small else F
     pred = (r * d + Fq * r) * e_p + 4 * Fq + B * d * e_x
     if spec.storage == "i4":
         rowb = d // 2 + 2 * (d // 128)
@@ -264,8 +265,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(spec.name, B) if not n_hot else None,
-                "kernel": "psffn_predict (k_h, k_q, k_list at B <= 4; the batch predictor kernels above): the "
-                          "fp16 predictor stream A then Q, threshold, mask words, ordered list",
+                "kernel": "psffn_predict (k_h, k_q, k_list on the small-batch pipeline; the batch predictor "
+                          "kernels where it runs): the predictor stream A then Q, threshold, mask words, "
+                          "ordered list",
                 "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
         del g_pred, g_ffn, idx_all
 

@@ -152,8 +152,9 @@ psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const voi
  * the predictor, which decides only for [n_hot, F).  The list is the ascending union of the two.
  *   n_hot   0 <= n_hot <= F (E_INVALID_ARG otherwise); 0 gives psffn_predict / psffn_layer exactly
  *   logits  as psffn_predict for neurons >= n_hot; the entries of hot neurons are unspecified
- * At B <= 4 the predictor does not read the Q rows of the hot prefix (F-n_hot rows stream
- * instead of F); larger batches compute every logit and force the prefix into the list.
+ * Where the small-batch predictor runs (fp32 predictors up to 4 tokens; fp16 ones at 1 token, and at
+ * 2 tokens up to 1024 ranks) it does not read the Q rows of the hot prefix (F-n_hot rows stream
+ * instead of F); the batch predictor computes every logit and forces the prefix into the list.
  * Everything else (arguments, outputs, workspace, errors) is as in psffn_predict / psffn_layer. */
 psffn_status psffn_predict_hot(const psffn_predictor* P, int n_hot, const void* x, int B, float logit_thr,
                                int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
