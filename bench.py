@@ -90,7 +90,8 @@ def main():
     ap.add_argument("--workload", default="opt30b_relu_f16")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=30,
+                    help="decode steps the CPU oracle baseline times (about 13 s of CPU work on the default layer)")
     ap.add_argument("--no-events", action="store_true", help="skip the per-call event pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 8 times with a plain device copy and exit (reference "
