@@ -248,7 +248,7 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
     e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
   } else if (!pb && !fb) {
     e = launch_layer_fused(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
-  } else if (pb) {
+  } else if (pb && ffn_fused_scan_fits(*W, B)) {
     // batch predictor up to its mask words, then the small-batch FFN orders the list from them (the
     // list the batch predictor's own list kernel would write, so the outputs equal the two calls)
     e = launch_predict_batch_masks(*P, x, B, logit_thr, logits, ws, stream);

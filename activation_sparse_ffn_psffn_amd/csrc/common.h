@@ -224,6 +224,7 @@ hipError_t launch_ffn_fused(St st, const psffn_ffn& W, const void* x, int B, con
                             float* y, int accumulate, void* ws, hipStream_t s);
 // the small-batch FFN from the mask words of a predictor call in the same workspace (the list and its
 // length are ordered inside the fused kernel and written to idx/count, as in launch_layer_fused)
+bool ffn_fused_scan_fits(const psffn_ffn& W, int B);  // launch_ffn_fused_scan can run this shape
 hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count,
                                  float* y, int accumulate, void* ws, hipStream_t s, int n_hot);
 // LayerNorm folded into the layer call (stack step): xres = the fp32 residual (the input of the

@@ -1159,6 +1159,17 @@ static hipError_t ffn_scan_nb(const psffn_ffn& W, const void* x, int B, int32_t*
   return hipErrorNotSupported;
 }
 
+bool ffn_fused_scan_fits(const psffn_ffn& W, int B) {
+  if (B < 1 || B > kFusedMaxBatch) return false;
+  const int NB = B == 1 ? 1 : (B == 2 ? 2 : 4);
+  const int NQ = (W.F + 31) / 32;
+  const size_t xe = W.dt == PSFFN_F32 ? 4 : 2;
+  const size_t ud = round256((size_t)B * W.d * xe) + round256(4 * (size_t)(2 * NQ + 1)) +
+                    4 * (size_t)kUDMaxRows * NB + 4 * (size_t)kUDMaxRows;
+  return W.F <= kUDSplitCap * kUDMaxRows && (size_t)B * W.d * xe <= (size_t)kStageX && NQ <= kMaxScanChunks &&
+         ud <= (size_t)150 * 1024;
+}
+
 hipError_t launch_ffn_fused_scan(St st, const psffn_ffn& W, const void* x, int B, int32_t* idx, int32_t* count,
                                  float* y, int accumulate, void* ws, hipStream_t s, int n_hot) {
   if (W.act == PSFFN_RELU) {
