@@ -44,6 +44,14 @@ def run_tokens(L, n, X, B, ntok_y=None, hot_first_perm=None):
     e2 = None
     if st["exact"]:
         e2 = check_y(y.cpu().numpy()[:tb], y_ref, tol)
+    # the one-call layer the benchmark times: the same list, count and output, bit for bit
+    logits2 = torch.empty(B, F, device=DEV)
+    idx2, count2, y2 = ps.layer(P, W, X, ws, logits=logits2)
+    torch.cuda.synchronize()
+    n_gpu = int(count.item())
+    assert torch.equal(logits2, logits)
+    assert int(count2.item()) == n_gpu and torch.equal(idx2[:n_gpu], idx[:n_gpu])
+    assert torch.equal(y2, y)
     say("  B=%d count=%d ref=%d in-band diffs=%d err(list)=%.2e err(end-to-end)=%s" % (
         B, st["count"], st["ref_count"], st["in_band_diff"], e1, "skipped" if e2 is None else "%.2e" % e2))
     return st
@@ -73,9 +81,12 @@ def test_opt30b_relu_f16_hot_first():
     assert torch.equal(W2.w_up, L.w_up) and torch.equal(W2.w_dT, L.w_dT) and torch.equal(P2.Q, L.Q)
     del W2, P2
     n = L.numpy()
-    X = synth.make_tokens(spec, 6, seed=0, device=DEV)
+    X = synth.make_tokens(spec, 10, seed=0, device=DEV)
     exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(6))
     assert exact >= 4
+    # two tokens (small-batch kernels) and four (batch pipeline)
+    run_tokens(L, n, X[6:8].contiguous(), 2, ntok_y=1)
+    run_tokens(L, n, X[6:10].contiguous(), 4, ntok_y=1)
     # the offline profile at full size, one token, bracketed by the oracle's counts at +-1e-4
     Xp = synth.make_tokens(spec, 1, seed=0, stream="profile", device=DEV)
     got = ps.profile_counts(ffn_of(L, ps), Xp).cpu().numpy()
@@ -89,23 +100,26 @@ def test_llama2_13b_swiglu_f16():
     say("generate", spec.name)
     L = synth.make_layer(spec, seed=0, device=DEV)
     n = L.numpy()
-    X = synth.make_tokens(spec, 3, seed=0, device=DEV)
+    X = synth.make_tokens(spec, 6, seed=0, device=DEV)
     exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(3))
     assert exact >= 2
+    # three tokens: the batch predictor with the small-batch FFN (one call ordering the list)
+    run_tokens(L, n, X[3:6].contiguous(), 3, ntok_y=1)
 
 
-def test_opt175b_relu_i4_batch1_and_batch8():
+def test_opt175b_relu_i4_batch1_2_and_8():
     spec = synth.CONFIGS["opt175b_relu_i4"]
     say("generate", spec.name)
     L = synth.make_layer(spec, seed=0, device=DEV)
     n = L.numpy()
     X = synth.make_tokens(spec, 10, seed=0, device=DEV)
     exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(2))
-    st = run_tokens(L, n, X[2:10].contiguous(), 8, ntok_y=2)
+    run_tokens(L, n, X[2:10].contiguous(), 8, ntok_y=2)
+    run_tokens(L, n, X[2:4].contiguous(), 2, ntok_y=1)  # 4-bit weights take the batch pipeline from 2 tokens
     assert exact >= 1
 
 
-@pytest.mark.parametrize("layer,B", [(0, 1), (47, 4), (23, 32)])
+@pytest.mark.parametrize("layer,B", [(0, 1), (11, 2), (47, 4), (23, 32)])
 def test_falcon40b_stack_layers(layer, B):
     spec = synth.CONFIGS["falcon40b_stack_f16"]
     say("generate", spec.name, "layer", layer, "density %.4f" % synth.layer_density(spec, 0, layer))
@@ -113,3 +127,17 @@ def test_falcon40b_stack_layers(layer, B):
     n = L.numpy()
     X = synth.make_tokens(spec, B, seed=layer, device=DEV)
     run_tokens(L, n, X, B, ntok_y=min(B, 2))
+    # the stack step the benchmark times (LayerNorm folded into the layer call where the small-batch
+    # pipeline runs) against the LayerNorm kernel followed by the layer call: the same bits
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    x0 = synth.make_residual(spec, B, seed=layer, device=DEV)
+    x1 = x0.clone()
+    h1 = ps.layernorm_f16(x1)
+    idx1, cnt1, _ = ps.layer(P, W, h1, ws, y=x1, accumulate=True)
+    x2 = x0.clone()
+    idx2, cnt2, h2 = ps.layer_ln(P, W, x2, ws)
+    torch.cuda.synchronize()
+    m = int(cnt1.item())
+    assert torch.equal(h1, h2) and torch.equal(x1, x2)
+    assert int(cnt2.item()) == m and torch.equal(idx1[:m], idx2[:m])
