@@ -202,6 +202,20 @@ __device__ void mask_prefix(const uint32_t* __restrict__ masks, int nq, int n_ho
   __syncthreads();
 }
 
+// The neuron at list position k (0 <= k < total): the last word q whose prefix count is <= k holds
+// it, as its (k - s_pre[q])-th set bit.
+__device__ __forceinline__ int list_at(const uint32_t* s_mask, const int* s_pre, int nq, int k) {
+  int lo = 0, hi = nq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_pre[mid] <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  uint32_t m = s_mask[lo];
+  for (int j = k - s_pre[lo]; j > 0; --j) m &= m - 1u;
+  return lo * 32 + (int)__builtin_ctz(m);
+}
+
 // =============================================================================================
 // k_bh: wave (row tile rt, chunk kc): partial h over d-elements [512 kc, 512 kc + 512) of rows
 // [16 rt, 16 rt + 16).  Grid (ceil(d / 512), ceil(r / 64)): consecutive workgroups read consecutive
@@ -672,8 +686,14 @@ template <> struct BUp<St::I4> { static constexpr int LPB = 1; };
 
 template <int KC>
 __host__ __device__ constexpr int bup_xpitch() { return KC * 2 + 16; }
+// bytes of LDS for the mask words and their prefix counts (scan mode of the up kernel)
+__host__ __device__ inline size_t bup_scan_lds(int nq) { return ((size_t)8 * nq + 4 + 15) / 16 * 16; }
 
-template <St WT, psffn_act ACT, int NT, int KC>
+// SCAN (the layer call): the list is not given; every workgroup builds the prefix counts of the
+// predictor's mask words in LDS (after the x chunk region) and each lane finds the neuron of its list
+// position itself.  The chunk-0 units write the list and workgroup 0 its length, for the kernels
+// that follow.
+template <St WT, psffn_act ACT, int NT, int KC, bool SCAN>
 __global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
   constexpr int NBP = 16 * NT;
   constexpr int KB = KC / 128;
@@ -687,7 +707,17 @@ __global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
   char* s_x = reinterpret_cast<char*>(s_dyn4);
   const int lane = wave_lane(), li = lane & 15, lg = lane >> 4, wv = wave_id();
   const int d = g.d;
-  const int n_list = blist_len(g.count, g.F);
+  int n_list;
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_x + NBP * XP);
+  int* s_pre = reinterpret_cast<int*>(s_mask + g.nq);
+  if constexpr (SCAN) {
+    __shared__ int s_red[kBlock / kWave];
+    mask_prefix<kBlock>(g.masks, g.nq, g.n_hot, s_mask, s_pre, s_red);
+    n_list = min(s_pre[g.nq], g.F);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *g.count_out = n_list;
+  } else {
+    n_list = blist_len(g.count, g.F);
+  }
   const int nrb = (n_list + 63) / 64;
   const int nkc = (d + KC - 1) / KC;
   const int units = nrb * nkc;
@@ -698,7 +728,13 @@ __global__ __launch_bounds__(kBlock) void k_bup(BArgs g) {
     // this lane's A row (list position) first, then the x chunk (rows n < NBP, elements
     // [KC kc, KC kc + KC), zero past B or d), then the weight rows once the neuron id is back
     const int k = rb * 64 + wv * 16 + li;
-    const int i_raw = g.idx[k < n_list ? k : n_list - 1];
+    int i_raw;
+    if constexpr (SCAN) {
+      i_raw = list_at(s_mask, s_pre, g.nq, k < n_list ? k : n_list - 1);
+      if (kc == 0 && k < n_list && lg == 0) g.idx_out[k] = i_raw;
+    } else {
+      i_raw = g.idx[k < n_list ? k : n_list - 1];
+    }
     uint4 xs[PPT];
 #pragma unroll
     for (int q = 0; q < PPT; ++q) {
@@ -1296,14 +1332,17 @@ static hipError_t pred_launch(const BArgs& g, hipStream_t s) {
 }
 
 template <St WT, psffn_act ACT, int NT>
-static void ffn_launch_b(const BArgs& g, hipStream_t s) {
+static void ffn_launch_b(const BArgs& g, hipStream_t s, bool scan) {
   constexpr int NBP = 16 * NT;
   constexpr int KC = (WT == St::I4 && NT == 1) ? 1024 : 512;
   const int nkc = (g.d + KC - 1) / KC;
   const size_t lds = (size_t)NBP * bup_xpitch<KC>();
   int units = ((g.F + 63) / 64) * nkc;
   if (units > 1024) units = 1024;
-  k_bup<WT, ACT, NT, KC><<<units, kBlock, lds, s>>>(g);
+  if (scan)
+    k_bup<WT, ACT, NT, KC, true><<<units, kBlock, lds + bup_scan_lds(g.nq), s>>>(g);
+  else
+    k_bup<WT, ACT, NT, KC, false><<<units, kBlock, lds, s>>>(g);
   int act_grid = (NBP * g.ldk + kBlock - 1) / kBlock;
   if (act_grid > 1024) act_grid = 1024;
   k_bact<ACT><<<act_grid, kBlock, 0, s>>>(g, nkc, NBP);
@@ -1316,18 +1355,30 @@ static void ffn_launch_b(const BArgs& g, hipStream_t s) {
 }
 
 template <St WT, psffn_act ACT>
-static void ffn_launch_nt(const BArgs& g, hipStream_t s) {
-  if (g.B <= 16) ffn_launch_b<WT, ACT, 1>(g, s);
-  else ffn_launch_b<WT, ACT, 2>(g, s);
+static void ffn_launch_nt(const BArgs& g, hipStream_t s, bool scan) {
+  if (g.B <= 16) ffn_launch_b<WT, ACT, 1>(g, s, scan);
+  else ffn_launch_b<WT, ACT, 2>(g, s, scan);
 }
 
-static void ffn_dispatch(const psffn_ffn& W, const BArgs& g, hipStream_t s) {
+// The layer call lets the up kernel order the list for fp16 weights (measured on MI355X, same box:
+// OPT-30B shape at 4 tokens 60.3 -> 55.4 us, 48-layer stack at 4 and 32 tokens +2.5% and +1.4%
+// tokens/s); for 4-bit weights the larger LDS footprint of their 1024-element x chunk costs more
+// than the list kernel (OPT-175B shape at 8 tokens 107.2 -> 108.4 us), so they keep it.  The LDS
+// (x chunk plus the mask words and their prefix counts) must fit the default 64 KB.
+static bool bup_scan_fits(const psffn_ffn& W, int B, int nq) {
+  if (W.dt != PSFFN_F16) return false;
+  const int NT = B <= 16 ? 1 : 2;
+  const int KC = (W.dt == PSFFN_I4G128 && NT == 1) ? 1024 : 512;
+  return (size_t)16 * NT * (KC * 2 + 16) + bup_scan_lds(nq) <= (size_t)64 * 1024;
+}
+
+static void ffn_dispatch(const psffn_ffn& W, const BArgs& g, hipStream_t s, bool scan = false) {
   if (W.dt == PSFFN_I4G128) {
-    if (W.act == PSFFN_RELU) ffn_launch_nt<St::I4, PSFFN_RELU>(g, s);
-    else ffn_launch_nt<St::I4, PSFFN_SWIGLU>(g, s);
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::I4, PSFFN_RELU>(g, s, scan);
+    else ffn_launch_nt<St::I4, PSFFN_SWIGLU>(g, s, scan);
   } else {
-    if (W.act == PSFFN_RELU) ffn_launch_nt<St::F16, PSFFN_RELU>(g, s);
-    else ffn_launch_nt<St::F16, PSFFN_SWIGLU>(g, s);
+    if (W.act == PSFFN_RELU) ffn_launch_nt<St::F16, PSFFN_RELU>(g, s, scan);
+    else ffn_launch_nt<St::F16, PSFFN_SWIGLU>(g, s, scan);
   }
 }
 
@@ -1377,10 +1428,22 @@ hipError_t launch_layer_batch(const psffn_predictor& P, const psffn_ffn& W, cons
   g.n_hot = n_hot;
   g.idx_out = idx;
   g.count_out = count;
-  hipError_t e = predict_and_scan(g, s);
-  if (e != hipSuccess) return e;
   BArgs f{};
   ffn_args_b(f, W, x, B, idx, count, y, accumulate, ws);
+  if (bup_scan_fits(W, B, g.nq)) {
+    // the up kernel orders the list from the mask words itself (no list kernel, one launch fewer)
+    const hipError_t e = g.B <= 16 ? pred_launch<1>(g, s) : pred_launch<2>(g, s);
+    if (e != hipSuccess) return e;
+    f.masks = g.masks;
+    f.nq = g.nq;
+    f.n_hot = n_hot;
+    f.idx_out = idx;
+    f.count_out = count;
+    ffn_dispatch(W, f, s, true);
+    return hipGetLastError();
+  }
+  hipError_t e = predict_and_scan(g, s);
+  if (e != hipSuccess) return e;
   ffn_dispatch(W, f, s);
   return hipGetLastError();
 }
