@@ -397,3 +397,34 @@ def test_layer_ln_needs_an_fp16_predictor():
     x = synth.make_residual(c["spec"], 1, seed=5, device=DEV, d=c["spec"].d).contiguous()
     with pytest.raises(ps.PsffnError):
         ps.layer_ln(c["P"], c["W"], x, c["ws"])
+
+
+@pytest.mark.parametrize("F,B", [(262144, 1), (262144, 2), (98304, 8), (98305, 8)])
+def test_largest_neuron_counts(F, B):
+    # F = 262144: the most neurons the small-batch layer path orders (8192 mask words, 256 splits
+    # of at most 1024 rows); F = 98304: the batch pipeline's limit; one more neuron: the generic
+    # kernels take over.  Narrow rows keep the oracle fast.
+    spec = spec_variant("opt30b_relu_f16", density=0.03)
+    say("largest F", F, "B", B)
+    L = synth.make_layer(spec, seed=2, device=DEV, d=64, F=F, r=16)
+    n = L.numpy()
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    X = synth.make_tokens(L.spec, B, seed=3, device=DEV, d=64)
+    Xn = X.cpu().numpy()
+    logits = torch.empty(B, F, device=DEV)
+    idx, cnt = ps.predict(P, X, ws, logits=logits)
+    y1 = ps.sparse_ffn(W, X, idx, cnt, ws)
+    idx2, cnt2, y2 = ps.layer(P, W, X, ws)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    st = check_set(idx, cnt, ref)
+    m = int(cnt.item())
+    assert int(cnt2.item()) == m and torch.equal(idx2[:m], idx[:m]) and torch.equal(y1, y2)
+    orc = oracle_layer(n, "relu")
+    lst = oracle.compact(ref)
+    y_o = ps.sparse_ffn(W, X, torch.from_numpy(lst).to(DEV), torch.tensor([len(lst)], dtype=torch.int32,
+                                                                          device=DEV), ws)
+    check_y(y_o.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
+    if st["exact"]:
+        check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
