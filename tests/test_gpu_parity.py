@@ -428,3 +428,41 @@ def test_largest_neuron_counts(F, B):
     check_y(y_o.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
     if st["exact"]:
         check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
+
+
+@pytest.mark.parametrize("d,B", [(32768, 1), (32776, 1), (16384, 4)])
+def test_widest_rows(d, B):
+    # B x d fp16 activations fill the small-batch kernels' 64 KB of LDS at d = 32768 (B = 1) and
+    # d = 16384 (B = 4); one slice more and the generic kernels take over.  The stack step at these
+    # widths takes the LayerNorm kernel (its in-kernel form covers d <= 16384).
+    spec = spec_variant("opt30b_relu_f16", density=0.05)
+    say("widest rows d", d, "B", B)
+    L = synth.make_layer(spec, seed=4, device=DEV, d=d, F=600, r=24)
+    n = L.numpy()
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    X = synth.make_tokens(L.spec, B, seed=5, device=DEV, d=d)
+    Xn = X.cpu().numpy()
+    idx, cnt = ps.predict(P, X, ws)
+    y1 = ps.sparse_ffn(W, X, idx, cnt, ws)
+    idx2, cnt2, y2 = ps.layer(P, W, X, ws)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    st = check_set(idx, cnt, ref)
+    m = int(cnt.item())
+    assert int(cnt2.item()) == m and torch.equal(idx2[:m], idx[:m]) and torch.equal(y1, y2)
+    lst = oracle.compact(ref)
+    orc = oracle_layer(n, "relu")
+    y_o = ps.sparse_ffn(W, X, torch.from_numpy(lst).to(DEV), torch.tensor([len(lst)], dtype=torch.int32,
+                                                                          device=DEV), ws)
+    check_y(y_o.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
+    if st["exact"]:
+        check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("f16"))
+    x0 = synth.make_residual(L.spec, B, seed=6, device=DEV, d=d)
+    x1 = x0.clone()
+    h1 = ps.layernorm_f16(x1)
+    ps.layer(P, W, h1, ws, y=x1, accumulate=True)
+    x2 = x0.clone()
+    _, _, h2 = ps.layer_ln(P, W, x2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(x1, x2)
