@@ -29,16 +29,14 @@ METRIC = "sparse-FFN µs/layer and achieved HBM GB/s (% of roofline) at batch 1"
 HBM_PEAK_GBPS = 8000.0
 
 
-# HBM bytes per predictor call (k_h + k_q), from two rocprofv3 --pmc passes over this script
-# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, averaged over the calls).  A plain device copy of
-# 512 MiB reads as 262156 KiB of FETCH_SIZE and 524288 KiB of WRITE_SIZE, so FETCH_SIZE is scaled
-# by 2.0 and WRITE_SIZE by 1.0.  A figure holds only for the kernel sources it was measured on
-# (hash below); after any change to them the traffic is reported as null until measured again.
+# HBM bytes per psffn_layer step (every kernel of the call), from two rocprofv3 --pmc passes over
+# this script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch, summed over the step's kernels and
+# averaged over the steps).  A plain device copy of 512 MiB reads as 262156 KiB of FETCH_SIZE and
+# 524288 KiB of WRITE_SIZE, so FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0.  A figure holds
+# only for the kernel sources it was measured on (hash below); after any change to them the
+# traffic is reported as null until measured again.
 TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/fused.hip")
-TRAFFIC = {
-    # (workload, batch): fetch KiB k_h 7263.0 + k_q 28831.1 + k_list 4.1, write KiB 8.0 + 28.0 + 3.4
-    ("opt30b_relu_f16", 1): {"sources": "70be07ca54453e62", "bytes": 73969668},
-}
+TRAFFIC = {}
 
 
 def sources_hash():
@@ -59,6 +57,40 @@ def measured_traffic(workload, B):
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def graph_plan(steps, graph_steps):
+    """Partition of the K timed steps into consecutive captured HIP graphs: (first step, length)
+    pairs covering [0, steps) in order.  Full graphs of graph_steps steps, then one shorter graph
+    for the remainder; graph_steps <= 0 means no graphs (eager launches: an empty plan)."""
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    if graph_steps <= 0:
+        return []
+    plan, t = [], 0
+    while t < steps:
+        n = min(graph_steps, steps - t)
+        plan.append((t, n))
+        t += n
+    return plan
+
+
+def host_cpu():
+    """(logical CPUs this process may use, CPU model name) of the host the bench runs on."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
 
 
 def algorithmic_bytes(spec, B, n_active, n_hot=0):
@@ -187,18 +219,16 @@ def main():
 
     # the timed region: K steps replayed from HIP graphs of G consecutive steps (distinct tokens,
     # rotating layer copies), so that host launch overhead is not part of the step
-    G = args.graph_steps
-    if G > 0:
-        if K % G:
-            raise SystemExit("--steps must be a multiple of --graph-steps")
+    plan = graph_plan(K, args.graph_steps)
+    graphs = []
+    if plan:
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
-        graphs = []
-        for g0 in range(0, K, G):
+        for g0, gn in plan:
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.stream(cap):
                 with torch.cuda.graph(gr, stream=cap):
-                    for t in range(g0, g0 + G):
+                    for t in range(g0, g0 + gn):
                         step(Wm + t, counts_all[t:t + 1], cap)
             graphs.append(gr)
         stream.wait_stream(cap)
@@ -209,7 +239,7 @@ def main():
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e_start.record(stream)
-    if G > 0:
+    if graphs:
         for gr in graphs:
             gr.replay()
     else:
@@ -261,16 +291,19 @@ def main():
         pred_us = ev[0].elapsed_time(ev[1]) * 1e3 / K
         ffn_us = ev[1].elapsed_time(ev[2]) * 1e3 / K
         breakdown = {"predict_us": round(pred_us, 3), "sparse_ffn_us": round(ffn_us, 3),
-                     "two_call_step_us": round(pred_us + ffn_us, 3)}
-        achieved = pred_bytes / (pred_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(spec.name, B) if not n_hot else None,
-                "kernel": "psffn_predict (k_h, k_q, k_list on the small-batch pipeline; the batch predictor "
-                          "kernels where it runs): the predictor stream A then Q, threshold, mask words, "
-                          "ordered list",
-                "bytes_per_launch": int(pred_bytes), "avg_launch_us": round(pred_us, 3)}
+                     "two_call_step_us": round(pred_us + ffn_us, 3),
+                     "predict_bytes": int(pred_bytes), "sparse_ffn_bytes": int(ffn_bytes),
+                     "predict_gbps": round(pred_bytes / (pred_us * 1e-6) / 1e9, 1),
+                     "sparse_ffn_gbps": round(ffn_bytes / (ffn_us * 1e-6) / 1e9, 1)}
         del g_pred, g_ffn, idx_all
+
+    # the roofline covers the timed launch sequence itself: one psffn_layer call per step, its
+    # algorithmic bytes over its average duration (HIP events on the stream the calls run on)
+    traffic = measured_traffic(spec.name, B) if not n_hot else None
+    roof = {"bound": "hbm", "achieved": round(layer_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": "psffn_layer (%s)" % layer_kernels(spec, B),
+            "bytes_per_launch": int(step_bytes), "avg_launch_us": round(us_per_step, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -294,6 +327,15 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def layer_kernels(spec, B):
+    """The kernels one psffn_layer call launches for this workload and batch (as the library picks
+    its pipeline: small-batch kernels at one token and for the shapes they take, MFMA batch
+    kernels otherwise)."""
+    if B == 1 or spec.storage == "f32":
+        return "k_h, k_q, k_ud, k_reduce_ud"
+    return "small-batch or MFMA batch kernels by batch size"
+
+
 def bench_stack(args, spec, ps, synth, np, torch):
     """Decode through a stack of FFN layers: per layer x <- x + FFN(fp16(LayerNorm(x))), the FFN
     restricted to the batch's predicted union set; one step moves B tokens through all layers.
@@ -313,7 +355,8 @@ def bench_stack(args, spec, ps, synth, np, torch):
     F, d = spec.F, spec.d
     idx = torch.empty(F, dtype=torch.int32, device=dev)
     cnts = torch.zeros(L, dtype=torch.int32, device=dev)
-    x = synth.make_residual(spec, B, seed=0, device=dev)
+    x0 = synth.make_residual(spec, B, seed=0, device=dev)
+    x = x0.clone()
     hbuf = torch.empty(B, d, dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -322,7 +365,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
             # x <- x + FFN(fp16(LayerNorm(x))) in one library call
             ps.layer_ln(P, W, x, ws, eps=1e-5, h=hbuf, idx=idx, count=cnts[l:l + 1], stream=st)
 
-    for _ in range(max(1, args.warmup // 16)):
+    for _ in range(max(1, args.warmup)):
         step(stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -334,7 +377,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
     stream.wait_stream(cap)
     g.replay()
     torch.cuda.synchronize()
-    K = max(1, args.steps // 16)
+    K = args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(K):
@@ -345,18 +388,58 @@ def bench_stack(args, spec, ps, synth, np, torch):
     tok_s = B / (ms * 1e-3)
     n = cnts.cpu().numpy().astype(np.float64)
     byt = sum(sum(algorithmic_bytes(spec, B, n[l])) for l in range(L))
+    gbps = byt / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "kernel": "psffn_layer_ln (%s), 48 calls per step" % layer_kernels(spec, B),
+            "bytes_per_launch": int(byt / L), "avg_launch_us": round(ms * 1e3 / L, 3)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_stack(spec, layers, x0, B, L)
     out = {"metric": "decode tokens/s through a stack of sparse FFN layers", "value": round(tok_s, 1),
            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
            "config": {"workload": "%s: %d layers d=%d F=%d r=%d f16 relu, batch %d, per-layer density U(0.02,0.10) "
                                   "Zipf(1.0), residual + LayerNorm between layers" % (spec.name, L, d, F, spec.r, B),
                       "batch": B},
-           "layer": {"us_per_layer": round(ms * 1e3 / L, 3), "gbps": round(byt / (ms * 1e-3) / 1e9, 1),
-                     "frac_of_hbm_peak": round(byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "layer": {"us_per_layer": round(ms * 1e3 / L, 3), "gbps": round(gbps, 1),
+                     "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "mean_union_active_per_layer": round(float(n.mean()), 1),
+                     "union_active_per_layer_min_max": [int(n.min()), int(n.max())],
                      "algorithmic_bytes_per_step": int(byt)},
-           "roofline": None, "cpu_baseline": None}
+           "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_stack(spec, layers, x0, B, L, budget_s=12.0):
+    """The oracle timed on this host on a bounded sample of the stack: layer by layer from the
+    stack's input (x <- x + FFN(fp16(LayerNorm(x))) per layer), until about budget_s seconds of CPU
+    work or every layer is done; the mean time per layer is scaled to the whole stack."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build()
+    g = lambda t: t.detach().cpu().numpy()
+    x = x0.cpu().numpy()
+    spent, done = 0.0, 0
+    for l in range(L):
+        P, W, _ = layers[l]
+        lay = [(g(P.A), g(P.Q), g(P.c), oracle.Layer(spec.act, g(W.w_up), g(W.w_dT), b_up=g(W.b_up)))]
+        t0 = time.perf_counter()
+        x = oracle.stack_step(lay, x)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    per_layer = spent / done
+    log("cpu baseline: %d of %d layers in %.2f s" % (done, L, spent))
+    nproc, model = host_cpu()
+    return {"value": round(B / (per_layer * L), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_nproc": nproc, "host_cpu": model,
+            "sample": "the first %d of %d layers at batch %d (LayerNorm, predict, compact, sparse FFN, residual), "
+                      "time per layer scaled to the %d-layer stack; single-threaded fp64 C (one of the host's %d "
+                      "logical CPUs)" % (done, L, B, L, nproc)}
 
 
 def set_stats(pred_idx, fired):
@@ -470,9 +553,11 @@ def cpu_baseline(spec, copy0, X, B, ntok):
         oracle.predicted_layer(A, Q, c, lay, Xn[t])
     dt = time.perf_counter() - t0
     log("cpu baseline: %d steps in %.2f s" % (ntok, dt))
+    nproc, model = host_cpu()
     return {"value": round(dt / ntok * 1e6, 1), "unit": "us/layer", "cores": 1, "kind": "oracle",
+            "host_nproc": nproc, "host_cpu": model,
             "sample": "%d decode steps (batch %d) of the same layer: predict, compact, sparse FFN; "
-                      "single-threaded fp64 C" % (ntok, B)}
+                      "single-threaded fp64 C (one of the host's %d logical CPUs)" % (ntok, B, nproc)}
 
 
 if __name__ == "__main__":

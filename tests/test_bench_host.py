@@ -1,0 +1,34 @@
+"""Host logic of bench.py (no GPU): the partition of the timed steps into captured HIP graphs and
+the host CPU record of the oracle baseline."""
+import pytest
+
+import bench
+
+
+@pytest.mark.parametrize("steps", [1, 5, 20, 63, 64, 65, 128, 1000, 1024])
+@pytest.mark.parametrize("graph_steps", [1, 7, 64, 2048])
+def test_graph_plan_covers_every_step_once(steps, graph_steps):
+    plan = bench.graph_plan(steps, graph_steps)
+    covered = [t for g0, n in plan for t in range(g0, g0 + n)]
+    assert covered == list(range(steps))
+    assert all(1 <= n <= graph_steps for _, n in plan)
+    # only the last graph may be shorter
+    assert all(n == graph_steps for _, n in plan[:-1])
+
+
+def test_graph_plan_driver_command():
+    # the driver runs `bench.py --gpus 1 --steps 20 --warmup 5` with the default graph size
+    assert bench.graph_plan(20, 64) == [(0, 20)]
+    assert bench.graph_plan(1024, 64) == [(64 * k, 64) for k in range(16)]
+    assert bench.graph_plan(100, 64) == [(0, 64), (64, 36)]
+
+
+def test_graph_plan_eager_and_errors():
+    assert bench.graph_plan(20, 0) == []
+    with pytest.raises(ValueError):
+        bench.graph_plan(0, 64)
+
+
+def test_host_cpu_record():
+    n, model = bench.host_cpu()
+    assert n >= 1 and isinstance(model, str) and model
