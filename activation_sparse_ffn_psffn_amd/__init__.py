@@ -65,6 +65,8 @@ _lib.psffn_layer_hot.restype = _i
 _lib.psffn_layer_hot.argtypes = [_P(_Predictor), _P(_FFN), _i, _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]
 _lib.psffn_layer_ln.restype = _i
 _lib.psffn_layer_ln.argtypes = [_P(_Predictor), _P(_FFN), _vp, _f, _vp, _i, _f, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.psffn_layer_noalloc.restype = _i
+_lib.psffn_layer_noalloc.argtypes = [_P(_Predictor), _P(_FFN), _vp, _i, _f, _vp, _vp, _vp, _vp, _i, _vp]
 _lib.psffn_profile_counts.restype = _i
 _lib.psffn_profile_counts.argtypes = [_P(_FFN), _vp, _i, _vp, _vp]
 _lib.psffn_permute_hot_first.restype = _i
@@ -75,6 +77,7 @@ _lib.psffn_layernorm_f16.argtypes = [_vp, _i, _i, _f, _vp, _vp]
 
 EXPORTED = ("psffn_status_str", "psffn_workspace_bytes", "psffn_workspace_init", "psffn_predict", "psffn_compact",
             "psffn_sparse_ffn", "psffn_layer", "psffn_predict_hot", "psffn_layer_hot", "psffn_layer_ln",
+            "psffn_layer_noalloc",
             "psffn_profile_counts",
             "psffn_permute_hot_first",
             "psffn_layernorm_f16")
@@ -244,6 +247,26 @@ def layer(P: Predictor, W: FFN, x: torch.Tensor, ws: torch.Tensor, thr: float = 
     _check(_lib.psffn_layer(ctypes.byref(sp), ctypes.byref(sw), _ptr(x), B, float(thr), _ptr(idx), _ptr(count),
                             _ptr(logits), _ptr(y), int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream)),
            "layer")
+    return idx, count, y
+
+
+def layer_noalloc(P: Predictor, W: FFN, x: torch.Tensor, thr: float = 0.0, idx: torch.Tensor = None,
+                  count: torch.Tensor = None, logits: torch.Tensor = None, y: torch.Tensor = None,
+                  accumulate: bool = False, stream=None):
+    """psffn_layer with the library's static per-GPU scratch instead of a workspace (no allocation
+    in the library; calls overlapping on one GPU race).  Returns (idx, count, y)."""
+    B = x.shape[0]
+    F = P.Q.shape[0]
+    if idx is None:
+        idx = torch.empty(F, dtype=torch.int32, device=x.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=x.device)
+    if y is None:
+        y = torch.empty(B, W.d, dtype=torch.float32, device=x.device)
+    sp, sw = P.struct(), W.struct()
+    _check(_lib.psffn_layer_noalloc(ctypes.byref(sp), ctypes.byref(sw), _ptr(x), B, float(thr), _ptr(idx),
+                                    _ptr(count), _ptr(logits), _ptr(y), int(bool(accumulate)), _stream(stream)),
+           "layer_noalloc")
     return idx, count, y
 
 

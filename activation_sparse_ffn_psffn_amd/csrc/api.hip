@@ -2,11 +2,39 @@
 // workspace layout, and dispatch to the launchers.  See include/psffn.h for the contract.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace psffn;
 
+// Scratch of psffn_layer_noalloc: the workspace of that call lives here, one copy per GPU (each
+// device holds its own instance of this array at its own address, for as long as the process runs).
+// Host code never uses the array's name as an address: it takes the device address of the current
+// GPU's copy from hipGetSymbolAddress once per device (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[PSFFN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch; on the first call for a device, the address is
+// looked up and the scratch cleared with the fill kernel on the caller's stream (no memset node).
+psffn_status noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PSFFN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PSFFN_E_HIP;
+    if (launch_fill_zero(p, PSFFN_NOALLOC_SCRATCH_BYTES, stream) != hipSuccess) return PSFFN_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PSFFN_OK;
+}
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -109,6 +137,22 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 psffn_status hip_status(hipError_t e) { return e == hipSuccess ? PSFFN_OK : PSFFN_E_HIP; }
+
+// every argument of a layer call except the workspace
+psffn_status layer_args_ok(const psffn_predictor* P, const psffn_ffn* W, int n_hot, const void* x, int B,
+                           float logit_thr, const int32_t* idx, const int32_t* count, const float* logits,
+                           const float* y) {
+  psffn_status st = check_pred(P);
+  if (st == PSFFN_OK) st = check_ffn(W);
+  if (st != PSFFN_OK) return st;
+  if (n_hot < 0 || n_hot > P->F) return PSFFN_E_INVALID_ARG;
+  if (P->F != W->F || P->d != W->d) return PSFFN_E_INVALID_ARG;
+  if ((P->dt == PSFFN_F32) != (W->dt == PSFFN_F32)) return PSFFN_E_UNSUPPORTED;
+  if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
+      !aligned(y, 4) || (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
+    return PSFFN_E_INVALID_ARG;
+  return PSFFN_OK;
+}
 
 }  // namespace
 
@@ -228,15 +272,8 @@ psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const voi
 psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n_hot, const void* x, int B,
                              float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y, int accumulate,
                              void* ws, size_t ws_bytes, hipStream_t stream) {
-  psffn_status st = check_pred(P);
-  if (st == PSFFN_OK) st = check_ffn(W);
+  psffn_status st = layer_args_ok(P, W, n_hot, x, B, logit_thr, idx, count, logits, y);
   if (st != PSFFN_OK) return st;
-  if (n_hot < 0 || n_hot > P->F) return PSFFN_E_INVALID_ARG;
-  if (P->F != W->F || P->d != W->d) return PSFFN_E_INVALID_ARG;
-  if ((P->dt == PSFFN_F32) != (W->dt == PSFFN_F32)) return PSFFN_E_UNSUPPORTED;
-  if (!batch_ok(B) || !x || !aligned(x, 16) || !idx || !aligned(idx, 4) || !count || !aligned(count, 4) || !y ||
-      !aligned(y, 4) || (logits && !aligned(logits, 4)) || logit_thr != logit_thr)
-    return PSFFN_E_INVALID_ARG;
   size_t need = pred_need(*P, B);
   const size_t f = ffn_need(*W, B);
   need = f > need ? f : need;
@@ -260,6 +297,22 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
   st = psffn_predict_hot(P, n_hot, x, B, logit_thr, idx, count, logits, ws, ws_bytes, stream);
   if (st != PSFFN_OK) return st;
   return psffn_sparse_ffn(W, x, B, idx, count, y, accumulate, ws, ws_bytes, stream);
+}
+
+psffn_status psffn_layer_noalloc(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B,
+                                 float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y,
+                                 int accumulate, hipStream_t stream) {
+  // every argument is checked before anything (the first call's clearing of the scratch included)
+  // is enqueued; the scratch this call needs (psffn_layer's workspace) must fit the static array
+  const psffn_status chk = layer_args_ok(P, W, 0, x, B, logit_thr, idx, count, logits, y);
+  if (chk != PSFFN_OK) return chk;
+  const size_t need = psffn_workspace_bytes(P, W, B);
+  if (need == 0 || need > (size_t)PSFFN_NOALLOC_SCRATCH_BYTES) return PSFFN_E_WORKSPACE;
+  void* ws = nullptr;
+  const psffn_status st = noalloc_scratch(stream, &ws);
+  if (st != PSFFN_OK) return st;
+  return psffn_layer(P, W, x, B, logit_thr, idx, count, logits, y, accumulate, ws,
+                     (size_t)PSFFN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 psffn_status psffn_layer_ln(const psffn_predictor* P, const psffn_ffn* W, float* x, float eps, void* h, int B,

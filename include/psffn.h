@@ -176,6 +176,23 @@ psffn_status psffn_layer_ln(const psffn_predictor* P, const psffn_ffn* W, float*
                             float logit_thr, int32_t* idx, int32_t* count, float* logits, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* psffn_layer without a workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The library
+ * allocates nothing here either: the workspace is a static device array of
+ * PSFFN_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds until the process
+ * ends.  The first call on a device looks up that device's copy and clears it with a fill kernel on
+ * the given stream.
+ *   Arguments, outputs and errors are those of psffn_layer (no hot prefix).  A shape whose
+ *   workspace (psffn_workspace_bytes(P, W, B)) exceeds PSFFN_NOALLOC_SCRATCH_BYTES is rejected with
+ *   PSFFN_E_WORKSPACE before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array, which keeps the last call's contents: calls that
+ *   overlap on one GPU (unordered streams, concurrent host threads) race and give undefined outputs;
+ *   calls ordered on one stream are independent of each other. */
+#define PSFFN_NOALLOC_SCRATCH_BYTES (64u << 20)
+psffn_status psffn_layer_noalloc(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B,
+                                 float logit_thr, int32_t* idx, int32_t* count, float* logits, float* y,
+                                 int accumulate, hipStream_t stream);
+
 /* Offline activation profile (Summary, 2nd paragraph: models are profiled offline):
  * counts[i] = number of the T tokens X [T][d] for which neuron i truly fires -- the ReLU
  * pre-activation W_up[i].x + b_up[i] > 0, or for SwiGLU the gate W_gate[i].x + b_gate[i] > 0.

@@ -205,3 +205,23 @@ def test_layer_ln_rejects_bad_arguments():
     assert call(eps=-1.0) == INVALID
     assert call(eps=float("nan")) == INVALID
     assert call(Bn=0) == INVALID
+
+
+def test_layer_noalloc_rejects_bad_arguments_and_large_shapes():
+    # every case fails validation or the scratch-size check, both before any HIP call
+    P, W = pred(F=1024), ffn(F=1024)
+    call = lambda P=P, W=W, x=None, Bn=1, idx=None, y=None: lib.psffn_layer_noalloc(
+        B(P), B(W), fake() if x is None else x, Bn, 0.0, fake() if idx is None else idx, fake(), None,
+        fake() if y is None else y, 0, None)
+    assert lib.psffn_layer_noalloc(None, B(W), fake(), 1, 0.0, fake(), fake(), None, fake(), 0, None) == INVALID
+    assert call(P=pred(F=2048)) == INVALID  # P and W describe different layers
+    assert call(P=pred(F=1024, dt=ps.PSFFN_F32)) == UNSUPPORTED  # fp32 predictor with fp16 weights
+    assert call(Bn=0) == INVALID
+    assert call(Bn=ps.MAX_BATCH + 1) == INVALID
+    assert call(x=A16 + 4) == INVALID
+    assert call(idx=A16 + 2) == INVALID
+    # a layer whose workspace exceeds the static scratch (PSFFN_NOALLOC_SCRATCH_BYTES = 64 MiB)
+    big_p = pred(d=12288, F=49152, r=1536)
+    big_w = ffn(d=12288, F=49152, dt=ps.PSFFN_I4G128)
+    assert lib.psffn_workspace_bytes(B(big_p), B(big_w), 32) > (64 << 20)
+    assert call(P=big_p, W=big_w, Bn=32) == WORKSPACE
