@@ -17,7 +17,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpsffn.so")
-SOURCES = ["api.hip", "predict.hip", "ffn.hip", "fused.hip", "batch.hip", "misc.hip"]
+SOURCES = ["api.hip", "predict.hip", "ffn.hip", "fused.hip", "batch.hip", "misc.hip", "stream.hip"]
 ARCH = "gfx950"
 
 

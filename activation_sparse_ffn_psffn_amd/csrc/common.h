@@ -238,6 +238,24 @@ hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, cons
                               int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
                               hipStream_t s, int n_hot = 0, const LnArgs& ln = LnArgs{});
 
+// k_h alone at one token (fp16 predictor), with the stack step's LayerNorm when ln.xres is set; it
+// also zeroes the nzero words at zero and the nzero2 words at zero2 (for the launch after it, which
+// ORs bits and counts into them)
+hipError_t launch_h_f16_b1(const psffn_predictor& P, const void* x, float* h, const LnArgs& ln, hipStream_t s,
+                           uint32_t* zero, int nzero, uint32_t* zero2, int nzero2);
+
+// streamed one-token pipeline (stream.hip; fp16 predictor, fp16 ReLU weights): the up rows ride on
+// the logits kernel, the down projection sums its split partials itself.  Scratch after the mask
+// words: stream_scratch bytes.  NotSupported outside the shapes the *_fits calls accept.
+size_t stream_scratch(int r, int F, int d);
+bool stream_ffn_fits(const psffn_ffn& W, int B);
+bool stream_layer_fits(const psffn_predictor& P, const psffn_ffn& W, int B, bool ln);
+hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* idx, const int32_t* count, float* y,
+                             int accumulate, void* ws, hipStream_t s);
+hipError_t launch_layer_stream(const psffn_predictor& P, const psffn_ffn& W, const void* x, float thr, int32_t* idx,
+                               int32_t* count, float* logits, float* y, int accumulate, void* ws, hipStream_t s,
+                               int n_hot, const LnArgs& ln);
+
 // batch pipeline (2 <= B <= 32, fp16 predictor, fp16 or 4-bit FFN weights) on MFMA tiles; the
 // same NotSupported convention.  Above kFusedMaxBatch tokens it is the only pipeline; from 2 to
 // kFusedMaxBatch tokens the calls choose per stage (pred_on_batch / ffn_on_batch in api.hip).

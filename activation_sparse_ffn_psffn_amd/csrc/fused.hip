@@ -24,6 +24,7 @@
 // Loads are unconditional wherever the compiler would otherwise branch around them: a lane with
 // nothing to load reads a 16-byte zero block instead.  A load behind a branch makes the compiler
 // wait for every outstanding load at the join, which serialises independent row streams.
+#include "chunk.h"
 #include "common.h"
 
 namespace psffn {
@@ -73,13 +74,17 @@ constexpr int kHThreads = 256;
 // stores the fp16 rows to hout for the FFN kernel.
 template <St PT, int NB, int LNK>
 __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, const void* __restrict__ x, int d, int r,
-                                              int nb, float* __restrict__ h, float eps, _Float16* __restrict__ hout) {
+                                              int nb, float* __restrict__ h, float eps, _Float16* __restrict__ hout,
+                                              uint32_t* __restrict__ zero = nullptr, int nzero = 0,
+                                              uint32_t* __restrict__ zero2 = nullptr, int nzero2 = 0) {
   constexpr int EPL = Tr<PT>::EPL;
   constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int UN = 16;
   extern __shared__ uint4 s_x[];  // B * d activations (dynamic size)
   const int lane = wave_lane();
   const int j = blockIdx.x * (kHThreads / kWave) + wave_id();
+  for (int k = blockIdx.x * kHThreads + threadIdx.x; k < nzero; k += gridDim.x * kHThreads) zero[k] = 0u;
+  for (int k = blockIdx.x * kHThreads + threadIdx.x; k < nzero2; k += gridDim.x * kHThreads) zero2[k] = 0u;
   const char* arow = reinterpret_cast<const char*>(A) + (size_t)(j < r ? j : 0) * d * ESZ;
   // this wave's row loads go out first, then the workgroup stages x (all tokens) in LDS
   uint4 w[UN];
@@ -140,99 +145,19 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
 // hot-first layer) are kept without a test: their Q rows are not read, their bits are set, and
 // their logits are left unspecified.
 
-// The chunk's active bits.  Chunks of 16 neurons write the halves of the 32-bit words (little
-// endian); an odd last chunk writes its whole word, so the unused upper half reads as zero.
-template <int ROWS>
-__device__ __forceinline__ void store_chunk_bits(uint32_t* masks, int q, int NQ, uint32_t bits) {
-  static_assert(ROWS == 32 || ROWS == 16, "chunks of 32 or 16 neurons");
-  if constexpr (ROWS == 32) {
-    masks[q] = bits;
-  } else if ((q & 1) == 0 && q == NQ - 1) {
-    masks[q >> 1] = bits;
-  } else {
-    reinterpret_cast<uint16_t*>(masks)[q] = (uint16_t)bits;
-  }
-}
-
 template <St PT, int NB, int RV, int RPW>
 __global__ __launch_bounds__(kBlock) void k_q(const void* __restrict__ Q, const float* __restrict__ c,
                                               const float* __restrict__ h, int r, int F, float thr, int nb,
                                               float* __restrict__ logits, int NQ, uint32_t* __restrict__ masks,
                                               int n_hot) {
-  constexpr int EPL = Tr<PT>::EPL;
-  constexpr int ESZ = Tr<PT>::ESZ;
   constexpr int ROWS = 4 * RPW;
-  __shared__ uint32_t s_mask[kBlock / kWave];
-  const int lane = wave_lane(), wv = wave_id();
   const int q = blockIdx.x;
   if ((q + 1) * ROWS <= n_hot) {  // the whole chunk is hot (and below F)
     if (threadIdx.x == 0) store_chunk_bits<ROWS>(masks, q, NQ, ROWS == 32 ? 0xffffffffu : 0xffffu);
     return;
   }
-  const int i0 = q * ROWS + wv * RPW;
-  uint4 qv[RPW][RV];
-#pragma unroll
-  for (int k = 0; k < RPW; ++k)
-#pragma unroll
-    for (int v = 0; v < RV; ++v) {
-      const int i = i0 + k, e = v * kWave * EPL + lane * EPL;
-      qv[k][v] = ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && i >= n_hot && e < r);
-    }
-  // h (all tokens, fp32, zero past r) goes through LDS once per workgroup: the four waves share it
-  constexpr int HR = RV * kWave * EPL;  // h elements per token covered by the lanes' slices
-  __shared__ float4 s_h[NB * HR / 4];
-  for (int k = threadIdx.x; k < NB * HR / 4; k += kBlock) {
-    const int b = k / (HR / 4), e = (k % (HR / 4)) * 4;  // r % 8 == 0: whole float4s
-    s_h[k] = b < nb && e < r ? *reinterpret_cast<const float4*>(h + (size_t)b * r + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
-  float hv[NB][RV][EPL];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int v = 0; v < RV; ++v) {
-      const int e = v * kWave * EPL + lane * EPL;
-      const float4 a0 = s_h[(b * HR + e) / 4];
-      hv[b][v][0] = a0.x; hv[b][v][1] = a0.y; hv[b][v][2] = a0.z; hv[b][v][3] = a0.w;
-      if constexpr (EPL == 8) {
-        const float4 a1 = s_h[(b * HR + e) / 4 + 1];
-        hv[b][v][4] = a1.x; hv[b][v][5] = a1.y; hv[b][v][6] = a1.z; hv[b][v][7] = a1.w;
-      }
-    }
-  uint32_t mask = 0;
-#pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int i = i0 + k;
-    const float ci = i < F ? c[i] : 0.f;
-    bool on = false;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      float acc = 0.f;
-#pragma unroll
-      for (int v = 0; v < RV; ++v) {
-        if constexpr (PT == St::F16) {
-          acc = dot8_f16_f32(qv[k][v], make_float4(hv[b][v][0], hv[b][v][1], hv[b][v][2], hv[b][v][3]),
-                             make_float4(hv[b][v][4], hv[b][v][5], hv[b][v][6], hv[b][v][7]), acc);
-        } else {
-          acc = fmaf(__uint_as_float(qv[k][v].x), hv[b][v][0], acc);
-          acc = fmaf(__uint_as_float(qv[k][v].y), hv[b][v][1], acc);
-          acc = fmaf(__uint_as_float(qv[k][v].z), hv[b][v][2], acc);
-          acc = fmaf(__uint_as_float(qv[k][v].w), hv[b][v][3], acc);
-        }
-      }
-      const float l = wave_sum(acc) + ci;
-      if (b < nb) {
-        on |= l > thr;
-        if (logits && lane == 0 && i < F) logits[(size_t)b * F + i] = l;
-      }
-    }
-    if ((on || i < n_hot) && i < F) mask |= 1u << k;
-  }
-  if (lane == 0) s_mask[wv] = mask;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    store_chunk_bits<ROWS>(masks, q, NQ,
-                           s_mask[0] | (s_mask[1] << RPW) | (s_mask[2] << (2 * RPW)) | (s_mask[3] << (3 * RPW)));
+  const uint32_t bits = q_chunk<PT, NB, RV, RPW>(Q, c, h, r, F, thr, nb, logits, n_hot, q);
+  if (threadIdx.x == 0) store_chunk_bits<ROWS>(masks, q, NQ, bits);
 }
 
 // =========================================================================================
@@ -1010,6 +935,27 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
                                                                                              0.f, nullptr);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
   k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
+  return hipGetLastError();
+}
+
+// k_h alone at one token for an fp16 predictor: h = A x, or with ln.xres the LayerNorm of the fp32
+// residual inside (its fp16 rows go to ln.hout) and h = A LN(x)
+hipError_t launch_h_f16_b1(const psffn_predictor& P, const void* x, float* h, const LnArgs& ln, hipStream_t s,
+                           uint32_t* zero, int nzero, uint32_t* zero2, int nzero2) {
+  if (P.dt != PSFFN_F16 || (size_t)P.d * 2 > (size_t)kStageX) return hipErrorNotSupported;
+  const size_t xbytes = round256((size_t)P.d * 2);
+  const int hgrid = (P.r + kHThreads / kWave - 1) / (kHThreads / kWave);
+  if (ln.xres == nullptr) {
+    k_h<St::F16, 1, 0><<<hgrid, kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, 1, h, 0.f, nullptr, zero, nzero, zero2, nzero2);
+  } else {
+    const int k = ln_k(P.d);
+    if (k == 1) k_h<St::F16, 1, 1><<<hgrid, kHThreads, xbytes, s>>>(P.A, ln.xres, P.d, P.r, 1, h, ln.eps, ln.hout, zero, nzero, zero2, nzero2);
+    else if (k == 2) k_h<St::F16, 1, 2><<<hgrid, kHThreads, xbytes, s>>>(P.A, ln.xres, P.d, P.r, 1, h, ln.eps, ln.hout, zero, nzero, zero2, nzero2);
+    else if (k == 4) k_h<St::F16, 1, 4><<<hgrid, kHThreads, xbytes, s>>>(P.A, ln.xres, P.d, P.r, 1, h, ln.eps, ln.hout, zero, nzero, zero2, nzero2);
+    else if (k == 8) k_h<St::F16, 1, 8><<<hgrid, kHThreads, xbytes, s>>>(P.A, ln.xres, P.d, P.r, 1, h, ln.eps, ln.hout, zero, nzero, zero2, nzero2);
+    else if (k == 16) k_h<St::F16, 1, 16><<<hgrid, kHThreads, xbytes, s>>>(P.A, ln.xres, P.d, P.r, 1, h, ln.eps, ln.hout, zero, nzero, zero2, nzero2);
+    else return hipErrorNotSupported;
+  }
   return hipGetLastError();
 }
 

@@ -89,7 +89,7 @@ def test_sparse_ffn_on_oracle_list(label, B):
 
 
 @pytest.mark.parametrize("label", [c[0] for c in CASES])
-@pytest.mark.parametrize("B", [2, 8, 20])
+@pytest.mark.parametrize("B", [1, 2, 8, 20])
 def test_edge_lists(label, B):
     c = setup_case(label)
     say("edge lists", label, "B", B)
@@ -170,7 +170,7 @@ def test_perfect_predictor_list_gives_dense(label):
 
 
 @pytest.mark.parametrize("label", ["f16_relu", "i4_relu", "f16_swiglu"])
-@pytest.mark.parametrize("B", [4, 12])
+@pytest.mark.parametrize("B", [1, 4, 12])
 def test_accumulate_and_determinism(label, B):
     c = setup_case(label)
     say("accumulate/determinism", label, "B", B)
