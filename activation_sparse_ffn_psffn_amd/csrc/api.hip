@@ -364,9 +364,7 @@ psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int3
 
 psffn_status psffn_permute_hot_first(const int32_t* counts, int F, int32_t* perm, const psffn_ffn* src,
                                      const psffn_ffn* dst, const psffn_predictor* psrc, const psffn_predictor* pdst,
-                                     void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
+                                     hipStream_t stream) {
   if (F <= 0 || !counts || !aligned(counts, 4) || !perm || !aligned(perm, 4)) return PSFFN_E_INVALID_ARG;
   if ((src == nullptr) != (dst == nullptr) || (psrc == nullptr) != (pdst == nullptr)) return PSFFN_E_INVALID_ARG;
   struct Job {

@@ -18,6 +18,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -91,6 +92,20 @@ def host_cpu():
     except OSError:
         pass
     return n, model
+
+
+def hot_prefix_len(counts, tokens, p_hot):
+    """Length of the hot prefix of a hot-first layer (the neurons computed without prediction): the
+    number of neurons whose profiled firing frequency counts[i] / tokens is at least p_hot.  counts
+    are in the layer's hot-first order, so these are exactly the first ones."""
+    if tokens < 1 or not (0.0 < p_hot <= 1.0):
+        raise ValueError("hot_prefix_len: tokens >= 1 and 0 < p_hot <= 1")
+    c = counts.detach().to("cpu").long()
+    need = math.ceil(p_hot * tokens - 1e-9)
+    n = int((c >= need).sum().item())
+    if n and int(c[:n].min().item()) < need:
+        raise ValueError("hot_prefix_len: counts are not in hot-first (descending) order")
+    return n
 
 
 def algorithmic_bytes(spec, B, n_active, n_hot=0):
@@ -183,7 +198,7 @@ def main():
         counts = ps.profile_counts(W, Xp)
         perm, W, P = ps.permute_hot_first(counts, W, P)
         if args.hot > 0:
-            n_hot = ps.hot_prefix_len(counts[perm.long()], T, args.hot)
+            n_hot = hot_prefix_len(counts[perm.long()], T, args.hot)
             log("hot prefix: %d neurons fire on >= %.3f of %d profile tokens" % (n_hot, args.hot, T))
         del Xp, L
     torch.cuda.synchronize()

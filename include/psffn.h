@@ -122,8 +122,10 @@ psffn_status psffn_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream)
 psffn_status psffn_predict(const psffn_predictor* P, const void* x, int B, float logit_thr, int32_t* idx,
                            int32_t* count, float* logits, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Threshold + compaction alone, on logits produced elsewhere: logits fp32 [B][F] ->
- * ascending idx [F] and count (same rules as psffn_predict). */
+/* Threshold + compaction alone (Summary, 2nd paragraph: the kernels compute the neurons the
+ * predictor keeps and skip the rest -- this call forms the kept list), on logits produced
+ * elsewhere: logits fp32 [B][F] -> ascending idx [F] and count (same rules as psffn_predict:
+ * neuron i is kept when logits[b][i] > logit_thr for at least one b). */
 psffn_status psffn_compact(const float* logits, int B, int F, float logit_thr, int32_t* idx, int32_t* count,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -139,8 +141,10 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
                               float* y, int accumulate, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* One decode step of one layer: psffn_predict followed by psffn_sparse_ffn on its list, with
- * the same outputs (idx ascending, count, optional logits, y) and the same requirements, in the
- * fewest launches (the list is ordered inside the FFN's first kernel instead of by the predictor).
+ * the same outputs (idx ascending, count, optional logits, y, bit for bit) and the same
+ * requirements, in the fewest launches: at one token with fp16 ReLU weights the up rows are
+ * computed inside the predictor's logits kernel and the list is written by the down projection;
+ * elsewhere the list is ordered inside the FFN's first kernel instead of by the predictor.
  * P and W must describe the same layer (same F and d); P->dt is fp32 exactly when W->dt is fp32. */
 psffn_status psffn_layer(const psffn_predictor* P, const psffn_ffn* W, const void* x, int B, float logit_thr,
                          int32_t* idx, int32_t* count, float* logits, float* y, int accumulate, void* ws,
@@ -199,7 +203,8 @@ psffn_status psffn_layer_noalloc(const psffn_predictor* P, const psffn_ffn* W, c
  * counts: int32 [F], overwritten.  T >= 1. */
 psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int32_t* counts, hipStream_t stream);
 
-/* Hot-first neuron order (Interesting ideas, I1: the most used parts go first).
+/* Hot-first neuron order (Interesting ideas, I1: the most used parts go first; Summary, 2nd
+ * paragraph: the neurons are profiled offline by how often they fire).
  *   counts  int32 [F] fire counts (e.g. from psffn_profile_counts)
  *   perm    out, int32 [F]: perm[k] = original neuron placed at position k, in descending
  *           count order, ties by ascending original index (stable)
@@ -210,10 +215,10 @@ psffn_status psffn_profile_counts(const psffn_ffn* W, const void* X, int T, int3
  *   psrc/pdst  predictors: pdst Q row k = psrc Q row perm[k], c likewise; A is not
  *           neuron-indexed and is not touched.
  * Either pair may be NULL to permute only the other.  Out-of-place: dst buffers must not
- * overlap src buffers.  Needs the workspace of psffn_workspace_bytes(psrc, src, 1). */
+ * overlap src buffers (E_INVALID_ARG otherwise).  Needs no workspace. */
 psffn_status psffn_permute_hot_first(const int32_t* counts, int F, int32_t* perm, const psffn_ffn* src,
                                      const psffn_ffn* dst, const psffn_predictor* psrc, const psffn_predictor* pdst,
-                                     void* ws, size_t ws_bytes, hipStream_t stream);
+                                     hipStream_t stream);
 
 /* Decode-stack glue: out_f16[b] = fp16(LayerNorm(x[b])) with gamma 1, beta 0, population
  * variance and the given eps; x is the fp32 residual stream [B][d] (any B >= 1, d % 4 == 0). */

@@ -146,18 +146,18 @@ def test_profile_and_layernorm_reject_bad_arguments():
 
 def test_permute_rejects_bad_arguments():
     W, W2 = ffn(), ffn()
-    assert lib.psffn_permute_hot_first(None, 1024, fake(), None, None, None, None, None, 0, None) == INVALID
-    assert lib.psffn_permute_hot_first(fake(), 0, fake(), None, None, None, None, None, 0, None) == INVALID
-    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), None, None, None, None, 0, None) == INVALID
-    assert lib.psffn_permute_hot_first(fake(), 512, fake(), B(W), B(W2), None, None, None, 0, None) == INVALID
+    assert lib.psffn_permute_hot_first(None, 1024, fake(), None, None, None, None, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 0, fake(), None, None, None, None, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), None, None, None, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 512, fake(), B(W), B(W2), None, None, None) == INVALID
     # destination overlapping the source
     W3 = ffn(w_up=W.w_up + 64)
-    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), B(W3), None, None, None, 0, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), B(W3), None, None, None) == INVALID
     # source has b_up but destination lacks it
     W4 = ffn(b_up=None)
-    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), B(W4), None, None, None, 0, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), B(W), B(W4), None, None, None) == INVALID
     P1, P2 = pred(), pred(r=64)
-    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), None, None, B(P1), B(P2), None, 0, None) == INVALID
+    assert lib.psffn_permute_hot_first(fake(), 1024, fake(), None, None, B(P1), B(P2), None) == INVALID
 
 
 def test_workspace_init_rejects_bad_arguments():
@@ -178,19 +178,6 @@ def test_hot_prefix_calls_reject_bad_prefix():
                                  None) == UNSUPPORTED
     assert lib.psffn_layer_hot(B(P), B(W), 4, fake(), 0, 0.0, fake(), fake(), None, fake(), 0, fake(), 1 << 34,
                                None) == INVALID
-
-
-def test_hot_prefix_len_from_profile_counts():
-    import torch
-    counts = torch.tensor([512, 512, 511, 507, 506, 300, 2, 0], dtype=torch.int32)
-    assert ps.hot_prefix_len(counts, 512, 0.99) == 4  # ceil(0.99 * 512) = 507
-    assert ps.hot_prefix_len(counts, 512, 1.0) == 2
-    assert ps.hot_prefix_len(counts, 512, 0.001) == 7
-    assert ps.hot_prefix_len(torch.zeros(5, dtype=torch.int32), 512, 0.5) == 0
-    with pytest.raises(ValueError):
-        ps.hot_prefix_len(torch.tensor([1, 9], dtype=torch.int32), 10, 0.5)  # not hot-first
-    with pytest.raises(ValueError):
-        ps.hot_prefix_len(counts, 512, 0.0)
 
 
 def test_layer_ln_rejects_bad_arguments():

@@ -32,3 +32,16 @@ def test_graph_plan_eager_and_errors():
 def test_host_cpu_record():
     n, model = bench.host_cpu()
     assert n >= 1 and isinstance(model, str) and model
+
+
+def test_hot_prefix_len_from_profile_counts():
+    import torch
+    counts = torch.tensor([512, 512, 511, 507, 506, 300, 2, 0], dtype=torch.int32)
+    assert bench.hot_prefix_len(counts, 512, 0.99) == 4  # ceil(0.99 * 512) = 507
+    assert bench.hot_prefix_len(counts, 512, 1.0) == 2
+    assert bench.hot_prefix_len(counts, 512, 0.001) == 7
+    assert bench.hot_prefix_len(torch.zeros(5, dtype=torch.int32), 512, 0.5) == 0
+    with pytest.raises(ValueError):
+        bench.hot_prefix_len(torch.tensor([1, 9], dtype=torch.int32), 10, 0.5)  # not hot-first
+    with pytest.raises(ValueError):
+        bench.hot_prefix_len(counts, 512, 0.0)
