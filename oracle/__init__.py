@@ -75,6 +75,8 @@ def _L():
         _lib.orc_sparse_ffn.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p, _i, _p]
         _lib.orc_fire_counts.restype = None
         _lib.orc_fire_counts.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _d, _p]
+        _lib.orc_pre_activations.restype = None
+        _lib.orc_pre_activations.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _i, _p, _i, _p]
         _lib.orc_hot_first_perm.restype = None
         _lib.orc_hot_first_perm.argtypes = [_p, _i, _p]
         _lib.orc_layernorm.restype = None
@@ -241,6 +243,17 @@ class Layer:
                              _ptr(self.s_gate), _ptr(self.b_up), _ptr(self.b_gate), _dense_code(X), _ptr(X),
                              X.shape[0], float(thr), _ptr(counts))
         return counts
+
+    def pre_activations(self, X):
+        """z [T][F] (float64): the deciding pre-activation of every neuron on every token (ReLU: up,
+        SwiGLU: gate), the quantity whose sign fire_counts counts."""
+        X = np.ascontiguousarray(np.atleast_2d(X))
+        T = X.shape[0]
+        z = np.empty((T, self.F), dtype=np.float64)
+        _L().orc_pre_activations(self.dt, self.act, self.d, self.F, _ptr(self.w_up), _ptr(self.s_up),
+                                 _ptr(self.w_gate), _ptr(self.s_gate), _ptr(self.b_up), _ptr(self.b_gate),
+                                 _dense_code(X), _ptr(X), T, _ptr(z))
+        return z
 
     def permuted(self, perm):
         """The same layer with its neurons reordered: new neuron k = old neuron perm[k]."""

@@ -224,6 +224,23 @@ void orc_fire_counts(int dt_w, int act, int d, int F, const void* w_up, const ui
   }
 }
 
+/* The deciding pre-activations themselves: z[t][i] = the ReLU pre-activation W_up[i].x_t + b_up[i],
+ * or for SwiGLU the gate W_gate[i].x_t + b_gate[i] (fp64, the stored weights decoded exactly) --
+ * the quantity whose sign orc_fire_counts counts, for tests that need its distance from zero. */
+void orc_pre_activations(int dt_w, int act, int d, int F, const void* w_up, const uint16_t* s_up, const void* w_gate,
+                         const uint16_t* s_gate, const float* b_up, const float* b_gate, int dt_x, const void* x,
+                         int T, double* z) {
+  const void* w = act == ORC_RELU ? w_up : w_gate;
+  const uint16_t* s = act == ORC_RELU ? s_up : s_gate;
+  const float* bias = act == ORC_RELU ? b_up : b_gate;
+  for (int t = 0; t < T; ++t)
+    for (int i = 0; i < F; ++i) {
+      double v = bias ? (double)bias[i] : 0.0;
+      for (int k = 0; k < d; ++k) v += weight_elem(dt_w, w, s, d, i, k) * dense_elem(dt_x, x, d, t, k);
+      z[(size_t)t * F + i] = v;
+    }
+}
+
 /* Hot-first order (Interesting ideas, I1: the most used parts go first / to the fastest
  * memory).  perm[k] = the neuron placed at position k: descending fire count, ties broken by
  * ascending original index (a stable order). */

@@ -78,3 +78,50 @@ def check_y(y, ref, tol):
     e = rel_inf(y, ref)
     assert e <= tol, "max relative error %.3e > %.1e" % (e, tol)
     return e
+
+
+def ln_bound(x, ref):
+    """Allowed |LN_gpu - LN_ref| per element (fp16 output of an fp32 LayerNorm against the fp64
+    oracle): one fp16 ulp of the result, plus what fp32 arithmetic cannot avoid near zero -- x - mean
+    rounds at eps32 (|x| + |mean|), divided by the row's sigma (a few roundings: factor 16)."""
+    x = np.asarray(x, dtype=np.float64)
+    ulp = np.spacing(np.abs(ref).astype(np.float16)).astype(np.float64)
+    eps32 = float(np.finfo(np.float32).eps)
+    slack = 16 * eps32 * (np.abs(x).max(axis=1) + np.abs(x.mean(axis=1))) / np.sqrt(x.var(axis=1) + 1e-5)
+    return ulp + slack[:, None]
+
+
+def dequant_rows(n: dict, name: str, d: int):
+    """The stored rows of w_<name> as float64 (4-bit rows decoded by the oracle's own decoder)."""
+    w = n["w_" + name]
+    if w.dtype == np.uint8:
+        return oracle.i4_dequant(w, n["s_" + name], d)
+    return w.astype(np.float64)
+
+
+def check_counts(got, orc, n: dict, X):
+    """GPU fire counts against the oracle's deciding pre-activations z (fp64).  The GPU forms each z
+    in fp32 from exact products (fp16 x fp16, 4-bit x fp16; fp32 products round once), summed per
+    lane over d/64 slices of the row and then over a 6-level butterfly, plus the bias: a summation
+    tree of depth at most k = d/64 + 8, so |z_gpu - z| <= gamma_k * (sum_k |w_k x_k| + |b|) with
+    gamma_k = k u / (1 - k u), u = 2^-24.  A token whose z lies within that margin of zero may count
+    either way; the count must lie between the two extremes, and equal the oracle's count for every
+    neuron with no such token.  Returns the number of neurons with an ambiguous token."""
+    X = np.asarray(X)
+    d = orc.d
+    branch = "up" if orc.act == oracle.RELU else "gate"
+    Wd = dequant_rows(n, branch, d)
+    bias = n["b_" + branch]
+    bias = np.zeros(orc.F) if bias is None else bias.astype(np.float64)
+    S = np.abs(Wd) @ np.abs(X.astype(np.float64)).T + np.abs(bias)[:, None]  # [F][T]
+    k = d / 64 + 8
+    u = 2.0 ** -24
+    margin = (k * u / (1 - k * u)) * S
+    z = orc.pre_activations(X).T  # [F][T]
+    lo = (z > margin).sum(axis=1)
+    hi = (z > -margin).sum(axis=1)
+    got = np.asarray(got)
+    assert np.all(lo <= got) and np.all(got <= hi), "fire counts outside the fp32-accumulation bracket"
+    exact = lo == hi
+    assert np.array_equal(got[exact], (z > 0).sum(axis=1)[exact])
+    return int((~exact).sum())

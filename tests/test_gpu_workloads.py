@@ -1,6 +1,7 @@
 """GPU parity at the full sizes of the five synthetic workloads, on sampled tokens the oracle can
-compute one by one: active sets (bit-exact outside the 1e-6 logit band), FFN outputs on the
-oracle's own lists, and end-to-end predict -> sparse FFN on every sampled token whose GPU set
+compute one by one (32 tokens at batch 1 for each single-layer workload): active sets (bit-exact
+outside the 1e-6 logit band; the tokens with a difference inside the band are counted), FFN outputs
+on the oracle's own lists, and end-to-end predict -> sparse FFN on every sampled token whose GPU set
 equals the oracle's set."""
 import numpy as np
 import pytest
@@ -8,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from helpers import check_set, check_y, ffn_of, oracle_layer, pred_of, tol_for
+from helpers import check_counts, check_set, check_y, ffn_of, oracle_layer, pred_of, tol_for
 
 pytestmark = pytest.mark.gpu
 
@@ -57,6 +58,16 @@ def run_tokens(L, n, X, B, ntok_y=None, hot_first_perm=None):
     return st
 
 
+def tokens_b1(L, n, X, ntok):
+    """run_tokens at batch 1 on the first ntok tokens; returns how many had the oracle's exact set
+    (the others differ only inside the logit band)."""
+    sts = [run_tokens(L, n, X[t:t + 1].contiguous(), 1) for t in range(ntok)]
+    exact = sum(st["exact"] for st in sts)
+    say("  %d tokens at batch 1: %d with the oracle's exact set, %d with differences inside the band "
+        "(%d neurons in all)" % (ntok, exact, ntok - exact, sum(st["in_band_diff"] for st in sts)))
+    return exact
+
+
 def test_tiny_relu_f32_all_tokens():
     spec = synth.CONFIGS["tiny_relu_f32"]
     L = synth.make_layer(spec, seed=0, device=DEV)
@@ -81,18 +92,17 @@ def test_opt30b_relu_f16_hot_first():
     assert torch.equal(W2.w_up, L.w_up) and torch.equal(W2.w_dT, L.w_dT) and torch.equal(P2.Q, L.Q)
     del W2, P2
     n = L.numpy()
-    X = synth.make_tokens(spec, 10, seed=0, device=DEV)
-    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(6))
-    assert exact >= 4
+    X = synth.make_tokens(spec, 40, seed=0, device=DEV)
+    exact = tokens_b1(L, n, X, 32)
+    assert exact >= 28
     # two tokens (small-batch kernels) and four (batch pipeline)
-    run_tokens(L, n, X[6:8].contiguous(), 2, ntok_y=1)
-    run_tokens(L, n, X[6:10].contiguous(), 4, ntok_y=1)
-    # the offline profile at full size, one token, bracketed by the oracle's counts at +-1e-4
+    run_tokens(L, n, X[32:34].contiguous(), 2, ntok_y=1)
+    run_tokens(L, n, X[34:38].contiguous(), 4, ntok_y=1)
+    # the offline profile at full size, one token, within the fp32-accumulation bracket
     Xp = synth.make_tokens(spec, 1, seed=0, stream="profile", device=DEV)
     got = ps.profile_counts(ffn_of(L, ps), Xp).cpu().numpy()
-    orc = oracle_layer(n, "relu")
-    lo, hi = orc.fire_counts(Xp.cpu().numpy(), 1e-4), orc.fire_counts(Xp.cpu().numpy(), -1e-4)
-    assert np.all(lo <= got) and np.all(got <= hi)
+    amb = check_counts(got, oracle_layer(n, "relu"), n, Xp.cpu().numpy())
+    say("  profile: neurons with the token inside the fp32 margin: %d of %d" % (amb, spec.F))
 
 
 def test_llama2_13b_swiglu_f16():
@@ -100,11 +110,11 @@ def test_llama2_13b_swiglu_f16():
     say("generate", spec.name)
     L = synth.make_layer(spec, seed=0, device=DEV)
     n = L.numpy()
-    X = synth.make_tokens(spec, 6, seed=0, device=DEV)
-    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(3))
-    assert exact >= 2
+    X = synth.make_tokens(spec, 35, seed=0, device=DEV)
+    exact = tokens_b1(L, n, X, 32)
+    assert exact >= 28
     # three tokens: the batch predictor with the small-batch FFN (one call ordering the list)
-    run_tokens(L, n, X[3:6].contiguous(), 3, ntok_y=1)
+    run_tokens(L, n, X[32:35].contiguous(), 3, ntok_y=1)
 
 
 def test_opt175b_relu_i4_batch1_2_and_8():
@@ -112,11 +122,11 @@ def test_opt175b_relu_i4_batch1_2_and_8():
     say("generate", spec.name)
     L = synth.make_layer(spec, seed=0, device=DEV)
     n = L.numpy()
-    X = synth.make_tokens(spec, 10, seed=0, device=DEV)
-    exact = sum(run_tokens(L, n, X[t:t + 1].contiguous(), 1)["exact"] for t in range(2))
-    run_tokens(L, n, X[2:10].contiguous(), 8, ntok_y=2)
-    run_tokens(L, n, X[2:4].contiguous(), 2, ntok_y=1)  # 4-bit weights take the batch pipeline from 2 tokens
-    assert exact >= 1
+    X = synth.make_tokens(spec, 40, seed=0, device=DEV)
+    exact = tokens_b1(L, n, X, 32)
+    run_tokens(L, n, X[32:40].contiguous(), 8, ntok_y=2)
+    run_tokens(L, n, X[32:34].contiguous(), 2, ntok_y=1)  # 4-bit weights take the batch pipeline from 2 tokens
+    assert exact >= 28
 
 
 @pytest.mark.parametrize("layer,B", [(0, 1), (11, 2), (47, 4), (23, 32)])

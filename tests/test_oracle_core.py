@@ -281,6 +281,12 @@ def test_fire_counts_match_numpy():
         assert np.array_equal(cnt, (z > 0).sum(axis=1).astype(np.int32))
         for t in (-0.3, 0.25):
             assert np.array_equal(lay.fire_counts(X, t), (z > t).sum(axis=1).astype(np.int32))
+        # the pre-activations themselves: numpy's fp64 product (a library routine), and the same
+        # signs the counts come from
+        za = lay.pre_activations(X)
+        assert za.shape == (X.shape[0], lay.F)
+        assert np.allclose(za, z.T, rtol=1e-12, atol=1e-12 * np.abs(z).max())
+        assert np.array_equal((za > 0).sum(axis=0).astype(np.int32), cnt)
 
 
 def test_compact_with_hot_prefix():
