@@ -105,6 +105,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
 // butterfly), the same whichever rows share the group.
 constexpr int kUQ = 4;
 constexpr int kRPG = 2;
+constexpr int kRun = 1;  // k_qu: runs of consecutive neurons per chunk (1: fully interleaved)
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every row: reads zeros
 
 struct UpSlices {
@@ -421,6 +422,32 @@ __device__ __forceinline__ void write_list(const uint32_t* masks, int nq, int32_
 }
 
 // =========================================================================================
+// k_h1: h = A x at one token without the LayerNorm, one single-wave workgroup per row of A: the
+// lane's 16-byte slices of the row and of x (u < UN, rows of up to UN * 512 fp16) are all requested
+// at once and x is read straight from L2 (no LDS copy, no barrier), so r small workgroups keep the
+// whole of A in flight.  The same per-lane order and wave sum as the small-batch k_h: the same h.
+// It also zeroes the nzero words at zero (the mask words k_qu ORs its bits into).
+template <int UN>
+__global__ __launch_bounds__(kWave) void k_h1(const _Float16* __restrict__ A, const _Float16* __restrict__ x, int d,
+                                              float* __restrict__ h, uint32_t* __restrict__ zero, int nzero) {
+  for (int k = blockIdx.x * kWave + threadIdx.x; k < nzero; k += gridDim.x * kWave) zero[k] = 0u;
+  const int j = blockIdx.x, lane = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t ra = row_rsrc(A, j, (uint32_t)d * 2);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(x), 0, d * 2, kRsrcWord3);
+  uint4 w[UN], xv[UN];
+#pragma unroll
+  for (int u = 0; u < UN; ++u) w[u] = bload16(ra, (uint32_t)(u * kWave + lane) * 16);
+#pragma unroll
+  for (int u = 0; u < UN; ++u) xv[u] = bload16(rx, (uint32_t)(u * kWave + lane) * 16);
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < UN; ++u)
+    if ((u * kWave + lane) * 8 < d) acc = dot8_f16(w[u], xv[u], acc);
+  acc = wave_sum(acc);
+  if (lane == 0) h[j] = acc;
+}
+
+// =========================================================================================
 // k_qu: the logits of chunk q (16 neurons q + NC k, the logits kernel's arithmetic: the same bits as
 // psffn_predict), their bits ORed into the mask words (zeroed by k_h), then the up rows of the kept
 // ones, kRPG at a time by the whole workgroup.  The chunks interleave over the neuron range, so the
@@ -446,10 +473,10 @@ template <int RV>
 __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   const int q = blockIdx.x;
   if (q == 0) zero_tickets(g.ctr, g.T);
-  const uint32_t m = q_chunk<St::F16, 1, RV, 4, true>(g.Q, g.c, g.h, g.r, g.F, g.thr, 1, g.logits, g.n_hot, q,
+  const uint32_t m = q_chunk<St::F16, 1, RV, 4, kRun>(g.Q, g.c, g.h, g.r, g.F, g.thr, 1, g.logits, g.n_hot, q,
                                                        g.NC);
   if (threadIdx.x < 16 && ((m >> threadIdx.x) & 1u)) {
-    const int i = q + g.NC * (int)threadIdx.x;
+    const int i = chunk_neuron<kRun, 4>(q, g.NC, (int)threadIdx.x);
     __hip_atomic_fetch_or(g.masks + (i >> 5), 1u << (i & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (m == 0u) return;  // (uniform: every thread holds the same bits)
@@ -462,7 +489,7 @@ __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   for (int j0 = 0; j0 < nset; j0 += kRPG) {
     int ids[kRPG];
 #pragma unroll
-    for (int r = 0; r < kRPG; ++r) ids[r] = j0 + r < nset ? q + g.NC * nth_bit(mu, j0 + r) : -1;
+    for (int r = 0; r < kRPG; ++r) ids[r] = j0 + r < nset ? chunk_neuron<kRun, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
     up_rows_load(g.w_up, g.d, ids, o, w);
     up_rows_finish(w, xv, ids, g.b_up, g.a, s_p);
   }
@@ -558,9 +585,14 @@ hipError_t launch_layer_stream(const psffn_predictor& P, const psffn_ffn& W, con
   const StreamBufs bf = stream_bufs(ws, W.F, W.d);
   uint32_t* masks = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + state_layout(P.F).masks);
   const int nq = (P.F + 31) / 32;
-  // k_h zeroes the mask words (k_qu ORs its bits into them)
-  hipError_t e = launch_h_f16_b1(P, x, bf.h, ln, s, masks, nq, nullptr, 0);
-  if (e != hipSuccess) return e;
+  // the first kernel zeroes the mask words (k_qu ORs its bits into them)
+  if (ln.xres == nullptr) {
+    k_h1<kUQ * 4><<<P.r, kWave, 0, s>>>(static_cast<const _Float16*>(P.A), static_cast<const _Float16*>(x), P.d, bf.h,
+                                         masks, nq);
+  } else {
+    const hipError_t e = launch_h_f16_b1(P, x, bf.h, ln, s, masks, nq, nullptr, 0);
+    if (e != hipSuccess) return e;
+  }
   QuArgs q{};
   q.Q = P.Q;
   q.c = P.c;

@@ -36,7 +36,8 @@ HBM_PEAK_GBPS = 8000.0
 # 524288 KiB of WRITE_SIZE, so FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0.  A figure holds
 # only for the kernel sources it was measured on (hash below); after any change to them the
 # traffic is reported as null until measured again.
-TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/fused.hip")
+TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/chunk.h",
+                   "activation_sparse_ffn_psffn_amd/csrc/fused.hip", "activation_sparse_ffn_psffn_amd/csrc/stream.hip")
 TRAFFIC = {}
 
 
@@ -346,6 +347,8 @@ def layer_kernels(spec, B):
     """The kernels one psffn_layer call launches for this workload and batch (as the library picks
     its pipeline: small-batch kernels at one token and for the shapes they take, MFMA batch
     kernels otherwise)."""
+    if B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
+        return "k_h, k_qu, k_dn"
     if B == 1 or spec.storage == "f32":
         return "k_h, k_q, k_ud, k_reduce_ud"
     return "small-batch or MFMA batch kernels by batch size"
