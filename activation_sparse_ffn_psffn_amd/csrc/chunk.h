@@ -19,23 +19,30 @@ __device__ __forceinline__ uint4 q_ld16z(const void* p, bool ok) {
   return *reinterpret_cast<const uint4*>(ok ? p : static_cast<const void*>(q_zero16));
 }
 
-// Chunk q of 4*RPW neurons, RPW per wave of a kBlock-thread workgroup.  RUN = 4*RPW (contiguous):
-// bit k of the chunk is neuron q*4*RPW + k.  RUN < 4*RPW (interleaved): the chunk is 4*RPW/RUN runs
-// of RUN consecutive neurons, run j starting at RUN*(q + NC*j) with NC = the number of chunks, so the
-// low-indexed hot neurons of a hot-first layer spread over many chunks while each run's Q rows stay
-// one contiguous stretch; bit k is neuron RUN*(q + NC*(k / RUN)) + k % RUN.
+// Chunk q of 4*RPW neurons, RPW per wave of a kBlock-thread workgroup.  ILV = 0 (contiguous): bit k
+// of the chunk is neuron q*4*RPW + k.  ILV > 0 (interleaved): the chunks form blocks of ILV chunks
+// (the last one possibly shorter, nb chunks), each block covering 4*RPW*nb consecutive neurons, and
+// chunk g of a block takes its neurons g, g + nb, g + 2 nb, ...  The low-indexed hot neurons of a
+// hot-first layer then spread over the first block's chunks, while a chunk's Q rows stay within one
+// block (a few MB) instead of spanning the whole matrix, which streamed measurably slower on MI355X.
 // All the chunk's Q row loads are issued first, h (fp32, [nb][r], zero past r) is staged in LDS
 // once per workgroup, then every lane forms its partial dot products and the wave sums them.  A
 // neuron's logit does not depend on which chunk computes it.
 // Neurons below n_hot are kept without a test (their Q rows are not read; their logits are
 // unspecified).  Writes the logits when asked, and returns the chunk's kept-neuron bits in every
 // thread.  Contains barriers: every thread of the workgroup calls it.
-template <int RUN, int RPW>
+template <int ILV, int RPW>
 __device__ __forceinline__ int chunk_neuron(int q, int NC, int k) {
-  return RUN == 4 * RPW ? q * 4 * RPW + k : RUN * (q + NC * (k / RUN)) + k % RUN;
+  if constexpr (ILV == 0) {
+    return q * 4 * RPW + k;
+  } else {
+    const int G = q / ILV, g = q - G * ILV;
+    const int nb = NC - G * ILV < ILV ? NC - G * ILV : ILV;
+    return G * ILV * 4 * RPW + g + nb * k;
+  }
 }
 
-template <St PT, int NB, int RV, int RPW, int RUN = 4 * RPW>
+template <St PT, int NB, int RV, int RPW, int ILV = 0>
 __device__ __forceinline__ uint32_t q_chunk(const void* __restrict__ Q, const float* __restrict__ c,
                                             const float* __restrict__ h, int r, int F, float thr, int nb,
                                             float* __restrict__ logits, int n_hot, int q, int NC = 0) {
@@ -48,7 +55,7 @@ __device__ __forceinline__ uint32_t q_chunk(const void* __restrict__ Q, const fl
   for (int k = 0; k < RPW; ++k)
 #pragma unroll
     for (int v = 0; v < RV; ++v) {
-      const int i = chunk_neuron<RUN, RPW>(q, NC, wv * RPW + k), e = v * kWave * EPL + lane * EPL;
+      const int i = chunk_neuron<ILV, RPW>(q, NC, wv * RPW + k), e = v * kWave * EPL + lane * EPL;
       qv[k][v] = q_ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && i >= n_hot && e < r);
     }
   // h (all tokens, fp32, zero past r) goes through LDS once per workgroup: the four waves share it
@@ -75,7 +82,7 @@ __device__ __forceinline__ uint32_t q_chunk(const void* __restrict__ Q, const fl
   uint32_t mask = 0;
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
-    const int i = chunk_neuron<RUN, RPW>(q, NC, wv * RPW + k);
+    const int i = chunk_neuron<ILV, RPW>(q, NC, wv * RPW + k);
     const float ci = i < F ? c[i] : 0.f;
     bool on = false;
 #pragma unroll

@@ -105,7 +105,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int
 // butterfly), the same whichever rows share the group.
 constexpr int kUQ = 4;
 constexpr int kRPG = 2;
-constexpr int kRun = 1;  // k_qu: runs of consecutive neurons per chunk (1: fully interleaved)
+constexpr int kIlv = 256;  // k_qu: chunks per interleave block (measured: 128 32.3, 256 32.0, 512 32.7,
+                           // the whole range 33.2, contiguous chunks 41.2 us on the OPT-30B-shaped layer)
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every row: reads zeros
 
 struct UpSlices {
@@ -448,11 +449,11 @@ __global__ __launch_bounds__(kWave) void k_h1(const _Float16* __restrict__ A, co
 }
 
 // =========================================================================================
-// k_qu: the logits of chunk q (16 neurons q + NC k, the logits kernel's arithmetic: the same bits as
-// psffn_predict), their bits ORed into the mask words (zeroed by k_h), then the up rows of the kept
-// ones, kRPG at a time by the whole workgroup.  The chunks interleave over the neuron range, so the
-// hot neurons of a hot-first layer (low indices) spread over all chunks and no workgroup is left with
-// a chunk of 16 hot rows.
+// k_qu: the logits of chunk q (16 neurons interleaved within a block of kIlv chunks: the logits
+// kernel's arithmetic, the same bits as psffn_predict), their bits ORed into the mask words (zeroed by
+// the kernel before), then the up rows of the kept ones, kRPG at a time by the whole workgroup.  The
+// interleave spreads the hot neurons of a hot-first layer (low indices) over the first block's
+// chunks, so no workgroup is left with a chunk of 16 hot rows.
 
 struct QuArgs {
   const void* Q;
@@ -473,10 +474,10 @@ template <int RV>
 __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   const int q = blockIdx.x;
   if (q == 0) zero_tickets(g.ctr, g.T);
-  const uint32_t m = q_chunk<St::F16, 1, RV, 4, kRun>(g.Q, g.c, g.h, g.r, g.F, g.thr, 1, g.logits, g.n_hot, q,
+  const uint32_t m = q_chunk<St::F16, 1, RV, 4, kIlv>(g.Q, g.c, g.h, g.r, g.F, g.thr, 1, g.logits, g.n_hot, q,
                                                        g.NC);
   if (threadIdx.x < 16 && ((m >> threadIdx.x) & 1u)) {
-    const int i = chunk_neuron<kRun, 4>(q, g.NC, (int)threadIdx.x);
+    const int i = chunk_neuron<kIlv, 4>(q, g.NC, (int)threadIdx.x);
     __hip_atomic_fetch_or(g.masks + (i >> 5), 1u << (i & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (m == 0u) return;  // (uniform: every thread holds the same bits)
@@ -489,7 +490,7 @@ __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   for (int j0 = 0; j0 < nset; j0 += kRPG) {
     int ids[kRPG];
 #pragma unroll
-    for (int r = 0; r < kRPG; ++r) ids[r] = j0 + r < nset ? chunk_neuron<kRun, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
+    for (int r = 0; r < kRPG; ++r) ids[r] = j0 + r < nset ? chunk_neuron<kIlv, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
     up_rows_load(g.w_up, g.d, ids, o, w);
     up_rows_finish(w, xv, ids, g.b_up, g.a, s_p);
   }

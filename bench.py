@@ -348,7 +348,7 @@ def layer_kernels(spec, B):
     its pipeline: small-batch kernels at one token and for the shapes they take, MFMA batch
     kernels otherwise)."""
     if B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
-        return "k_h, k_qu, k_dn"
+        return "k_h1, k_qu, k_dn"
     if B == 1 or spec.storage == "f32":
         return "k_h, k_q, k_ud, k_reduce_ud"
     return "small-batch or MFMA batch kernels by batch size"

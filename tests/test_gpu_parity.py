@@ -20,6 +20,9 @@ DEV = "cuda"
 CASES = [
     ("f32_relu", "tiny_relu_f32", dict(d=264, F=1000, r=40)),
     ("f16_relu", "opt30b_relu_f16", dict(d=1288, F=2000, r=136, density=0.05)),
+    # more neurons than one interleave block of the one-token layer's logits kernel (256 chunks of 16),
+    # with a ragged last block
+    ("f16_relu_blocks", "opt30b_relu_f16", dict(d=776, F=5000, r=64, density=0.05)),
     ("f16_swiglu", "llama2_13b_swiglu_f16", dict(d=1032, F=1500, r=72)),
     ("i4_relu", "opt175b_relu_i4", dict(d=1152, F=1200, r=64, density=0.08)),
     ("i4_swiglu", "opt175b_relu_i4", dict(d=640, F=700, r=32, act="swiglu", density=0.4)),
