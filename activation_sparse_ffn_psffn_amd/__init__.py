@@ -20,7 +20,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpsffn.so")
+# PSFFN_LIB names another build of the same library (the host-sanitizer test loads one whose host code
+# is built with ASan + UBSan); there is no fallback when the library is missing
+LIB_PATH = os.environ.get("PSFFN_LIB") or os.path.join(_HERE, "libpsffn.so")
 
 PSFFN_OK, PSFFN_E_INVALID_ARG, PSFFN_E_UNSUPPORTED, PSFFN_E_WORKSPACE, PSFFN_E_HIP = range(5)
 PSFFN_F32, PSFFN_F16, PSFFN_I4G128 = 0, 1, 2

@@ -1,6 +1,7 @@
 // extern "C" boundary of libpsffn: argument validation (host only, before anything is enqueued),
 // workspace layout, and dispatch to the launchers.  See include/psffn.h for the contract.
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -38,6 +39,16 @@ psffn_status noalloc_scratch(hipStream_t stream, void** out) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+// An enum field as the int a C caller stored in it (any value: reading a C++ enum object that holds a
+// value outside the enumeration's range would be undefined behaviour, so it is copied out as bytes).
+template <class E>
+int enum_value(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized here");
+  int v;
+  memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 St st_of(psffn_dtype dt) { return dt == PSFFN_F32 ? St::F32 : (dt == PSFFN_F16 ? St::F16 : St::I4); }
 
 size_t elem_row_bytes(psffn_dtype dt, int n) {
@@ -50,7 +61,8 @@ psffn_status check_pred(const psffn_predictor* P) {
   if (!P) return PSFFN_E_INVALID_ARG;
   if (P->d <= 0 || P->F <= 0 || P->r <= 0) return PSFFN_E_INVALID_ARG;
   if (P->d > kMaxD || P->r > kMaxD) return PSFFN_E_UNSUPPORTED;
-  if (P->dt != PSFFN_F32 && P->dt != PSFFN_F16) return PSFFN_E_UNSUPPORTED;
+  const int dt = enum_value(P->dt);
+  if (dt != PSFFN_F32 && dt != PSFFN_F16) return PSFFN_E_UNSUPPORTED;
   if (P->d % 8 != 0 || P->r % 8 != 0) return PSFFN_E_UNSUPPORTED;
   if (!P->A || !P->Q || !P->c) return PSFFN_E_INVALID_ARG;
   if (!aligned(P->A, 16) || !aligned(P->Q, 16) || !aligned(P->c, 4)) return PSFFN_E_INVALID_ARG;
@@ -61,8 +73,9 @@ psffn_status check_ffn(const psffn_ffn* W) {
   if (!W) return PSFFN_E_INVALID_ARG;
   if (W->d <= 0 || W->F <= 0) return PSFFN_E_INVALID_ARG;
   if (W->d > kMaxD) return PSFFN_E_UNSUPPORTED;
-  if (W->dt != PSFFN_F32 && W->dt != PSFFN_F16 && W->dt != PSFFN_I4G128) return PSFFN_E_UNSUPPORTED;
-  if (W->act != PSFFN_RELU && W->act != PSFFN_SWIGLU) return PSFFN_E_UNSUPPORTED;
+  const int dt = enum_value(W->dt), act = enum_value(W->act);
+  if (dt != PSFFN_F32 && dt != PSFFN_F16 && dt != PSFFN_I4G128) return PSFFN_E_UNSUPPORTED;
+  if (act != PSFFN_RELU && act != PSFFN_SWIGLU) return PSFFN_E_UNSUPPORTED;
   if (W->dt == PSFFN_I4G128 ? (W->d % 128 != 0) : (W->d % 8 != 0)) return PSFFN_E_UNSUPPORTED;
   if (!W->w_up || !W->w_dT) return PSFFN_E_INVALID_ARG;
   if (!aligned(W->w_up, 16) || !aligned(W->w_dT, 16)) return PSFFN_E_INVALID_ARG;
@@ -159,7 +172,7 @@ psffn_status layer_args_ok(const psffn_predictor* P, const psffn_ffn* W, int n_h
 extern "C" {
 
 const char* psffn_status_str(psffn_status s) {
-  switch (s) {
+  switch (enum_value(s)) {
     case PSFFN_OK: return "ok";
     case PSFFN_E_INVALID_ARG: return "invalid argument";
     case PSFFN_E_UNSUPPORTED: return "unsupported dtype/activation/shape combination";

@@ -34,6 +34,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "psffn_oracle.c")
 _LIB = os.path.join(_HERE, "_psffn_oracle.so")
+# a separately built copy of the same source (the host-sanitizer test builds one with ASan + UBSan)
+_LIB_OVERRIDE = os.environ.get("PSFFN_ORACLE_LIB")
 
 F32, F16, I4G128 = 0, 1, 2
 RELU, SWIGLU = 0, 1
@@ -55,7 +57,7 @@ _lib = None
 def _L():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        _lib = ctypes.CDLL(_LIB_OVERRIDE if _LIB_OVERRIDE else build())
         _p, _i, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         _lib.orc_half_to_double.restype = _d
         _lib.orc_half_to_double.argtypes = [ctypes.c_uint16]
