@@ -148,10 +148,13 @@ def main():
                     help="hot prefix: neurons profiled to fire on at least this fraction of the profile tokens "
                          "are computed without prediction (psffn_layer_hot); the layer is profiled and permuted "
                          "hot-first first.  0 = off")
-    ap.add_argument("--study", default="", choices=["", "predictor"],
+    ap.add_argument("--study", default="", choices=["", "predictor", "sizing", "drift"],
                     help="predictor: accuracy and speed of predictors aligned with the layer (rank-r "
                          "approximations of the deciding weights) at several ranks, against the generated one")
     ap.add_argument("--ranks", default="128,256,512,1024", help="ranks of the aligned predictors (--study)")
+    ap.add_argument("--sizing-tokens", type=int, default=16, help="calibration tokens per layer (--study sizing)")
+    ap.add_argument("--sizing-price", type=float, default=1.0,
+                    help="--study sizing: MB of predictor worth spending to find one more firing neuron per token")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="steps per captured HIP graph in the timed region (0: eager launches)")
     args = ap.parse_args()
@@ -184,6 +187,10 @@ def main():
     torch.cuda.init()
     if args.study == "predictor":
         return bench_study(args, spec, ps, synth, np, torch)
+    if args.study == "sizing":
+        return bench_sizing(args, spec, ps, synth, np, torch)
+    if args.study == "drift":
+        return bench_drift(args, spec, ps, synth, np, torch)
     if spec.layers > 1:
         return bench_stack(args, spec, ps, synth, np, torch)
     log("workload", spec.name, "B", B)
@@ -363,8 +370,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
     layers = []
     for l in range(L):
         Ly = synth.make_layer(spec, seed=0, layer=l, device=dev)
-        layers.append((ps.Predictor(Ly.A, Ly.Q, Ly.c), ps.FFN(spec.act, Ly.w_up, Ly.w_dT, b_up=Ly.b_up),
-                       float(Ly.p.sum())))
+        layers.append((ps.Predictor(Ly.A, Ly.Q, Ly.c), ps.FFN(spec.act, Ly.w_up, Ly.w_dT, b_up=Ly.b_up), Ly.p))
         del Ly
     torch.cuda.synchronize()
     log("stack of %d layers ready in %.1f s" % (L, time.time() - t0))
@@ -406,6 +412,8 @@ def bench_stack(args, spec, ps, synth, np, torch):
     tok_s = B / (ms * 1e-3)
     n = cnts.cpu().numpy().astype(np.float64)
     byt = sum(sum(algorithmic_bytes(spec, B, n[l])) for l in range(L))
+    # the union a batch of B independent tokens would have: sum_i 1 - (1 - p_i)^B per layer
+    exp_union = [float((1.0 - (1.0 - pl) ** B).sum()) for (_, _, pl) in layers]
     gbps = byt / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
@@ -424,6 +432,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "mean_union_active_per_layer": round(float(n.mean()), 1),
                      "union_active_per_layer_min_max": [int(n.min()), int(n.max())],
+                     "mean_union_if_tokens_independent": round(float(np.mean(exp_union)), 1),
                      "algorithmic_bytes_per_step": int(byt)},
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
@@ -474,6 +483,146 @@ def cosine(a, b):
     b = np.asarray(b, np.float64).ravel()
     na, nb = np.linalg.norm(a), np.linalg.norm(b)
     return float(a @ b / (na * nb)) if na > 0 and nb > 0 else float(na == nb)
+
+
+def bench_drift(args, spec, ps, synth, np, torch):
+    """Drift of the decode stack from the oracle (reported, not graded): the GPU chain (psffn_layer_ln
+    per layer) and the oracle's own chain (oracle.stack_step, fp64) from the same x0, one layer at a
+    time, with ||x_gpu - x_oracle||inf / ||x_oracle||inf and the two sets' symmetric difference after
+    every layer (a set may differ inside the logit band, and the chains then go their own ways)."""
+    import oracle
+
+    B, dev, L = args.batch, "cuda", spec.layers
+    x0 = synth.make_residual(spec, B, seed=7, device=dev)
+    x = x0.clone()
+    xr = x0.cpu().numpy()
+    g = lambda t: t.detach().cpu().numpy()
+    rows = []
+    t0 = time.time()
+    for l in range(L):
+        Ly = synth.make_layer(spec, seed=0, layer=l, device=dev)
+        P, W = ps.Predictor(Ly.A, Ly.Q, Ly.c), ps.FFN(spec.act, Ly.w_up, Ly.w_dT, b_up=Ly.b_up)
+        ws = ps.new_workspace(P, W, B)
+        idx, cnt, h = ps.layer_ln(P, W, x, ws)
+        torch.cuda.synchronize()
+        gpu_set = g(idx[:int(cnt.item())])
+        A, Q, c = g(Ly.A), g(Ly.Q), g(Ly.c)
+        orc = oracle.Layer(spec.act, g(Ly.w_up), g(Ly.w_dT), b_up=g(Ly.b_up))
+        h_ref = oracle.round_to_f16(oracle.layernorm(xr))
+        ref_set = oracle.compact(oracle.predict_logits(A, Q, c, h_ref))
+        xr = oracle.stack_step([(A, Q, c, orc)], xr)
+        xg = g(x).astype(np.float64)
+        drift = float(np.abs(xg - xr).max() / max(np.abs(xr).max(), 1e-30))
+        rows.append({"layer": l, "rel_drift": drift, "set_sym_diff": int(len(np.setxor1d(gpu_set, ref_set))),
+                     "count": int(len(gpu_set))})
+        log("layer %2d drift %.3e set diff %d (%d listed)" % (l, drift, rows[-1]["set_sym_diff"], len(gpu_set)))
+        del Ly, P, W, ws, orc, A, Q, c
+    print(json.dumps({"study": "decode-stack drift from the oracle", "workload": spec.name, "layers": L, "batch": B,
+                      "final_rel_drift": rows[-1]["rel_drift"], "max_rel_drift": max(r["rel_drift"] for r in rows),
+                      "seconds": round(time.time() - t0, 1), "per_layer": rows}), flush=True)
+
+
+def bench_sizing(args, spec, ps, synth, np, torch):
+    """Per-layer predictor sizing for the decode stack (Elamur summary, Interesting ideas I3: each
+    layer's predictor is sized by that layer's sparsity and skew).
+
+    For every layer: the predictor aligned with the layer (synth.make_aligned_predictor) at the
+    configured rank r_max, and its leading-r truncations for r in --ranks; recall of the predicted set
+    against the neurons that truly fire, on --sizing-tokens calibration tokens (psffn_predict and
+    psffn_profile_counts on each token).  The layer's rank r_l grows from the smallest rank tried to
+    the next while the firing neurons the larger predictor additionally finds per token,
+    (recall(r') - recall(r)) x the layer's mean firing count, are worth its extra bytes at a price of
+    --sizing-price MB of predictor per neuron found: a layer with more firing neurons (lower
+    sparsity) or firing spread over more neurons (lower skew) gains more from a larger predictor and
+    gets one, a sparse, skewed layer keeps a small one.  Then the whole stack
+    (x <- x + FFN(fp16(LN(x))), psffn_layer_ln per layer, one HIP graph per step) is timed with the
+    aligned predictors at r_max and at r_l, and both are reported with the recall they give."""
+    B, dev, L = args.batch, "cuda", spec.layers
+    d, F = spec.d, spec.F
+    ranks = sorted({int(v) for v in args.ranks.split(",") if v} | {spec.r})
+    T = args.sizing_tokens
+    Xc = synth.make_tokens(spec, T, seed=1, stream="profile", device=dev).reshape(T, 1, d)
+    t0 = time.time()
+    layers, rows = [], []
+    for l in range(L):
+        Ly = synth.make_layer(spec, seed=0, layer=l, device=dev)
+        W = ps.FFN(spec.act, Ly.w_up, Ly.w_dT, b_up=Ly.b_up)
+        A, Q, c = synth.make_aligned_predictor(Ly, spec.r, seed=l)
+        if l == 0:
+            ws = ps.new_workspace(ps.Predictor(A, Q, c), W, max(B, 1))
+        fired = [ps.profile_counts(W, Xc[t]).cpu().numpy() > 0 for t in range(T)]
+        n_fire = float(np.mean([f.sum() for f in fired]))
+        rec = {}
+        preds = {}
+        for r in ranks:
+            P = ps.Predictor(A[:r].contiguous(), Q[:, :r].contiguous(), c)
+            preds[r] = P
+            vals = []
+            for t in range(T):
+                idx, cnt = ps.predict(P, Xc[t], ws)
+                vals.append(set_stats(idx[:int(cnt.item())].cpu().numpy(), fired[t])[0])
+            rec[r] = float(np.mean(vals))
+        r_l = ranks[0]
+        for r_next in ranks[1:]:
+            found = (rec[r_next] - rec[r_l]) * n_fire  # extra firing neurons found per token
+            cost_mb = (r_next - r_l) * (d + F) * 2 / 1e6  # extra predictor bytes (fp16 A rows + Q columns)
+            if found * args.sizing_price < cost_mb:
+                break
+            r_l = r_next
+        layers.append((preds[spec.r], preds[r_l], W))
+        rows.append({"layer": l, "density": round(synth.layer_density(spec, 0, l), 4), "rank": r_l,
+                     "mean_firing": round(n_fire, 1),
+                     "recall_by_rank": {str(r): round(v, 4) for r, v in rec.items()}})
+        log("layer %2d density %.4f recall %s -> rank %d" % (l, rows[-1]["density"], rows[-1]["recall_by_rank"], r_l))
+        del Ly, A, Q
+    log("sizing done in %.1f s" % (time.time() - t0))
+    x0 = synth.make_residual(spec, B, seed=0, device=dev)
+    hbuf = torch.empty(B, d, dtype=torch.float16, device=dev)
+    idx = torch.empty(F, dtype=torch.int32, device=dev)
+    cnts = torch.zeros(L, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(which):
+        x = x0.clone()
+
+        def step(st):
+            for l, lay in enumerate(layers):
+                ps.layer_ln(lay[which], lay[2], x, ws, eps=1e-5, h=hbuf, idx=idx, count=cnts[l:l + 1], stream=st)
+
+        step(stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step(cap)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        K = max(1, min(args.steps, 64))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return B / (e0.elapsed_time(e1) / K * 1e-3)
+
+    tok_full, tok_sized = timed(0), timed(1)
+    esz = 2
+    pbytes = lambda r: (r * d + F * r) * esz + 4 * F
+    full_b = sum(pbytes(spec.r) for _ in range(L))
+    sized_b = sum(pbytes(rw["rank"]) for rw in rows)
+    out = {"study": "per-layer predictor sizing (aligned predictors)", "workload": spec.name, "layers": L, "batch": B,
+           "calibration_tokens": T, "price_mb_per_neuron": args.sizing_price, "ranks_tried": ranks,
+           "ranks": [rw["rank"] for rw in rows], "densities": [rw["density"] for rw in rows],
+           "mean_recall_at_rmax": round(float(np.mean([rw["recall_by_rank"][str(spec.r)] for rw in rows])), 4),
+           "mean_recall_sized": round(float(np.mean([rw["recall_by_rank"][str(rw["rank"])] for rw in rows])), 4),
+           "predictor_bytes_per_step_rmax": full_b, "predictor_bytes_per_step_sized": sized_b,
+           "tokens_per_s_rmax": round(tok_full, 1), "tokens_per_s_sized": round(tok_sized, 1), "per_layer": rows}
+    print(json.dumps(out), flush=True)
 
 
 def bench_study(args, spec, ps, synth, np, torch):

@@ -28,8 +28,8 @@ def say(*a):
     print(*a, flush=True)
 
 
-def gpu_layer(layer):
-    L = synth.make_layer(SPEC, seed=0, layer=layer, device=DEV)
+def gpu_layer(layer, r=None):
+    L = synth.make_layer(SPEC, seed=0, layer=layer, device=DEV, r=r)
     return L, ffn_of(L, ps), pred_of(L, ps)
 
 
@@ -37,10 +37,13 @@ def orc_tuple(n):
     return (n["A"], n["Q"], n["c"], oracle_layer(n, "relu"))
 
 
-@pytest.mark.parametrize("layer,B", [(0, 1), (47, 4), (23, 32)])
-def test_stack_step_against_oracle(layer, B):
-    say("stack step", "layer", layer, "B", B, "density %.4f" % synth.layer_density(SPEC, 0, layer))
-    L, W, P = gpu_layer(layer)
+# (layer, batch, predictor rank): the configured rank 1024, and per-layer ranks as a sized stack
+# uses them (the rank changes only the predictor's shapes)
+@pytest.mark.parametrize("layer,B,r", [(0, 1, None), (47, 4, None), (23, 32, None), (5, 1, 128), (9, 1, 384),
+                                       (13, 4, 640)])
+def test_stack_step_against_oracle(layer, B, r):
+    say("stack step", "layer", layer, "B", B, "rank", r or SPEC.r, "density %.4f" % synth.layer_density(SPEC, 0, layer))
+    L, W, P = gpu_layer(layer, r)
     n = L.numpy()
     ws = ps.new_workspace(P, W, B)
     x0 = synth.make_residual(SPEC, B, seed=100 + layer, device=DEV)
@@ -81,15 +84,16 @@ def test_stack_step_against_oracle(layer, B):
 
 
 def test_four_layer_chain_drift():
-    # the GPU chain and the oracle's own chain from the same x0 (no teacher forcing): the drift is
-    # reported, not graded, since a set difference inside the logit band (or one fp16 ulp of a
-    # LayerNorm output) is a legitimate divergence that later layers carry on
-    B, layers = 1, [0, 1, 2, 3]
+    # a variable-rank stack (per-layer predictor ranks as a sized stack uses them): the GPU chain and
+    # the oracle's own chain from the same x0 (no teacher forcing); the drift is reported, not graded,
+    # since a set difference inside the logit band (or one fp16 ulp of a LayerNorm output) is a
+    # legitimate divergence that later layers carry on
+    B, layers, ranks = 1, [0, 1, 2, 3], [1024, 128, 384, 640]
     x0 = synth.make_residual(SPEC, B, seed=7, device=DEV)
     x = x0.clone()
     x_ref = x0.cpu().numpy()
-    for layer in layers:
-        L, W, P = gpu_layer(layer)
+    for layer, r in zip(layers, ranks):
+        L, W, P = gpu_layer(layer, r)
         n = L.numpy()
         ws = ps.new_workspace(P, W, B)
         ps.layer_ln(P, W, x, ws)
@@ -97,6 +101,6 @@ def test_four_layer_chain_drift():
         x_ref = oracle.stack_step([orc_tuple(n)], x_ref)
         xg = x.cpu().numpy()
         drift = rel_inf(xg, x_ref)
-        say("  after layer %d: ||x_gpu - x_oracle||inf / ||x_oracle||inf = %.2e" % (layer, drift))
+        say("  after layer %d (rank %d): ||x_gpu - x_oracle||inf / ||x_oracle||inf = %.2e" % (layer, r, drift))
         assert np.isfinite(xg).all() and drift < 1.0
         del L, W, P, ws, n
