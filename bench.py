@@ -38,7 +38,10 @@ HBM_PEAK_GBPS = 8000.0
 # traffic is reported as null until measured again.
 TRAFFIC_SOURCES = ("activation_sparse_ffn_psffn_amd/csrc/common.h", "activation_sparse_ffn_psffn_amd/csrc/chunk.h",
                    "activation_sparse_ffn_psffn_amd/csrc/fused.hip", "activation_sparse_ffn_psffn_amd/csrc/stream.hip")
-TRAFFIC = {}
+TRAFFIC = {
+    # profiles/opt30b_relu_f16_b1_hbm_traffic.md: k_h1 + k_qu + k_dn, 1.038x the algorithmic bytes
+    ("opt30b_relu_f16", 1): {"sources": "3a4c19cf9086de2e", "bytes": 101966438},
+}
 
 
 def sources_hash():
