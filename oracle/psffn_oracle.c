@@ -82,11 +82,19 @@ uint16_t orc_double_to_half(double v) {
   return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024));
 }
 
+/* The value of every binary16 bit pattern, filled once from orc_half_to_double when the library
+ * loads, so that reading an fp16 element is a lookup rather than a libm call. */
+static double half_value[65536];
+
+__attribute__((constructor)) static void fill_half_values(void) {
+  for (int h = 0; h < 65536; ++h) half_value[h] = orc_half_to_double((uint16_t)h);
+}
+
 /* Element (row, col) of a dense row-major matrix with `ld` columns, stored as fp32 or fp16. */
 static double dense_elem(int dt, const void* p, size_t ld, size_t row, size_t col) {
   size_t at = row * ld + col;
   if (dt == ORC_F32) return (double)((const float*)p)[at];
-  return orc_half_to_double(((const uint16_t*)p)[at]);
+  return half_value[((const uint16_t*)p)[at]];
 }
 
 /* Element (row, col) of a 4-bit weight matrix with `d` columns.  Reading of the format
@@ -98,7 +106,7 @@ double orc_i4_elem(const uint8_t* packed, const uint16_t* scales, size_t d, size
   uint8_t byte = packed[row * (d / 2) + col / 2];
   int nib = (col & 1) ? (byte >> 4) : (byte & 15);
   int q = nib >= 8 ? nib - 16 : nib;
-  double s = orc_half_to_double(scales[row * (d / 128) + col / 128]);
+  double s = half_value[scales[row * (d / 128) + col / 128]];
   return (double)q * s;
 }
 
@@ -194,12 +202,16 @@ void orc_sparse_ffn(int dt_w, int act, int d, int F, const void* w_up, const uin
   (void)F;
   double* a = (double*)malloc(sizeof(double) * ((size_t)count * B + 1));
   orc_activations(dt_w, act, d, w_up, s_up, w_gate, s_gate, b_up, b_gate, dt_x, x, B, idx, count, a);
-  for (int b = 0; b < B; ++b)
-    for (int j = 0; j < d; ++j) {
-      double s = b_down ? (double)b_down[j] : 0.0;
-      for (int k = 0; k < count; ++k) s += a[(size_t)k * B + b] * weight_elem(dt_w, w_dT, s_dT, d, idx[k], j);
-      y[(size_t)b * d + j] = s;
+  /* every y[b][j] starts at b_down[j] and takes the listed neurons' terms in list order; the terms
+   * are added row by row (one W_down^T row at a time) so the rows are read in memory order */
+  for (int b = 0; b < B; ++b) {
+    double* yb = y + (size_t)b * d;
+    for (int j = 0; j < d; ++j) yb[j] = b_down ? (double)b_down[j] : 0.0;
+    for (int k = 0; k < count; ++k) {
+      const double ak = a[(size_t)k * B + b];
+      for (int j = 0; j < d; ++j) yb[j] += ak * weight_elem(dt_w, w_dT, s_dT, d, idx[k], j);
     }
+  }
   free(a);
 }
 
