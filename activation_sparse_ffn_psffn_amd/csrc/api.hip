@@ -263,7 +263,8 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
   const St wt = st_of(W->dt);
   hipError_t e = hipErrorNotSupported;
   if (ffn_on_batch(*W, B)) e = launch_ffn_batch(*W, x, B, idx, count, y, accumulate, ws, stream);
-  else if (stream_ffn_fits(*W, B)) e = launch_ffn_stream(*W, x, idx, count, y, accumulate, ws, stream);
+  else if (stream_ffn_fits(*W, B) || stream_ffn_i4_fits(*W, B))
+    e = launch_ffn_stream(*W, x, idx, count, y, accumulate, ws, stream);
   if (e == hipErrorNotSupported && B <= kFusedMaxBatch)
     e = launch_ffn_fused(wt, *W, x, B, idx, count, y, accumulate, ws, stream);
   if (e == hipErrorNotSupported) {
@@ -296,7 +297,7 @@ psffn_status psffn_layer_hot(const psffn_predictor* P, const psffn_ffn* W, int n
   hipError_t e = hipErrorNotSupported;
   const bool pb = pred_on_batch(*P, B), fb = ffn_on_batch(*W, B);
   if (!pb && !fb && stream_layer_fits(*P, *W, B, false) && stream_scratch(P->r, P->F, P->d) <= need) {
-    // one token, fp16 ReLU: up rows inside the logits kernel, the split sum inside the down kernel
+    // one token, fp16 or 4-bit ReLU: up rows inside the logits kernel, the split sum inside the down kernel
     e = launch_layer_stream(*P, *W, x, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot, LnArgs{});
   } else if (pb && fb) {
     e = launch_layer_batch(*P, *W, x, B, logit_thr, idx, count, logits, y, accumulate, ws, stream, n_hot);
@@ -358,7 +359,7 @@ psffn_status psffn_layer_ln(const psffn_predictor* P, const psffn_ffn* W, float*
   const bool small = B <= kFusedMaxBatch && !pred_on_batch(*P, B) && !ffn_on_batch(*W, B);
   if (small && stream_layer_fits(*P, *W, B, true) && stream_scratch(P->r, P->F, P->d) <= need) {
     e = launch_layer_stream(*P, *W, h, logit_thr, idx, count, logits, x, 1, ws, stream, 0, ln);
-  } else if (small) {
+  } else if (small && !stream_ffn_i4_fits(*W, B)) {
     e = launch_layer_fused(*P, *W, h, B, logit_thr, idx, count, logits, x, 1, ws, stream, 0, ln);
   }
   if (e != hipErrorNotSupported) return hip_status(e);

@@ -296,12 +296,13 @@ __global__ __launch_bounds__(kBlock) void k_bhred(BArgs g, int ksh, int nbp) {
   const int n = t / g.r;
   float s = 0.f;
   if (n < g.B) {
-    for (int k0 = 0; k0 < ksh; k0 += 8) {
-      float v[8];
+    constexpr int kR = 32;  // chunk partials in flight per round (one round up to d = 16384)
+    for (int k0 = 0; k0 < ksh; k0 += kR) {
+      float v[kR];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = k0 + u < ksh ? g.hpart[(size_t)(k0 + u) * nbp * g.r + t] : 0.f;
+      for (int u = 0; u < kR; ++u) v[u] = k0 + u < ksh ? g.hpart[(size_t)(k0 + u) * nbp * g.r + t] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < kR; ++u)
         if (k0 + u < ksh) s += v[u];
     }
   }
@@ -868,24 +869,26 @@ __global__ __launch_bounds__(kBlock) void k_bact(BArgs g, int nkc, int nbp) {
     const int n = t / kpad, k = t % kpad;
     float a = 0.f;
     if (k < n_list && n < g.B) {
+      // the neuron id (for its biases) and the chunk partials are requested together
       const int i = g.idx[k];
-      if ((unsigned)i < (unsigned)g.F) {
-        float su = 0.f, sg = 0.f;
-        for (int c0 = 0; c0 < nkc; c0 += 8) {
-          float pu[8], pg[8];
+      constexpr int kR = 16;  // chunk partials in flight per round (one round up to 16 chunks)
+      float su = 0.f, sg = 0.f;
+      for (int c0 = 0; c0 < nkc; c0 += kR) {
+        float pu[kR], pg[kR];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const size_t o = ((size_t)(c0 + q) * nbp + n) * g.ldk + k;
-            pu[q] = c0 + q < nkc ? g.upart[o] : 0.f;
-            pg[q] = (ACT == PSFFN_SWIGLU && c0 + q < nkc) ? g.gpart[o] : 0.f;
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (c0 + q < nkc) {
-              su += pu[q];
-              if constexpr (ACT == PSFFN_SWIGLU) sg += pg[q];
-            }
+        for (int q = 0; q < kR; ++q) {
+          const size_t o = ((size_t)(c0 + q) * nbp + n) * g.ldk + k;
+          pu[q] = c0 + q < nkc ? g.upart[o] : 0.f;
+          pg[q] = (ACT == PSFFN_SWIGLU && c0 + q < nkc) ? g.gpart[o] : 0.f;
         }
+#pragma unroll
+        for (int q = 0; q < kR; ++q)
+          if (c0 + q < nkc) {
+            su += pu[q];
+            if constexpr (ACT == PSFFN_SWIGLU) sg += pg[q];
+          }
+      }
+      if ((unsigned)i < (unsigned)g.F) {
         su += g.b_up ? g.b_up[i] : 0.f;
         if constexpr (ACT == PSFFN_SWIGLU) {
           sg += g.b_gate ? g.b_gate[i] : 0.f;

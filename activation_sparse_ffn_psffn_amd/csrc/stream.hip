@@ -37,6 +37,10 @@ namespace {
 constexpr int kTile = 512;      // output columns per k_dn workgroup (1 KB of an fp16 row, 16 B per lane)
 constexpr int kSeg = 8;         // ids per thread per segment of k_dn's id gathering
 constexpr int kDnRB = 8;        // rows per wave in flight in k_dn
+constexpr int kCPL4 = 8;        // output columns per lane of the 4-bit k_dn (kCPL4 / 2 bytes of a row)
+constexpr int kTile4 = kWave * kCPL4;  // output columns per 4-bit k_dn workgroup
+constexpr int kDn4RB = 8;       // 4-bit rows per wave in flight in k_dn
+constexpr int kUQ4 = 2;         // 32-element slices per lane per 4-bit up row: rows of up to 16384 elements
 constexpr int kMaxWords = 8192;  // mask words the layer call takes (F <= 262144)
 constexpr int kSW = 1;         // k_dn splits: 32 kSW (split s: neurons i with i mod 32 kSW == s)
 constexpr int kMaxSplits = 32 * kSW;
@@ -237,7 +241,8 @@ struct DnArgs {
   const int32_t* idx;     // LIST
   const int32_t* count;
   const float* a;
-  const _Float16* w_dT;
+  const void* w_dT;       // fp16 rows of d, or 4-bit rows of d/2 bytes
+  const uint16_t* s_dT;   // 4-bit: fp16 scales [F][d/128]
   const float* b_down;
   float* part;            // [S][d]
   uint32_t* ctr;          // [T] tickets, kTicketStride apart
@@ -245,23 +250,31 @@ struct DnArgs {
   int d, F, T, accumulate;
 };
 
-template <bool LIST>
+template <bool LIST, bool I4>
 __device__ __forceinline__ void dn_split(const DnArgs& g, int t, int s) {
-  static_assert(kBlock * kSeg == (kBlock / kWave) * kTile, "the id list and the wave sums share one buffer");
-  __shared__ float s_buf[kBlock * kSeg];  // the segment's ids, then (after the rows) the four wave sums
+  constexpr int CPL = I4 ? kCPL4 : 8;    // output columns per lane
+  constexpr int TILE = kWave * CPL;      // kTile (fp16) or kTile4 (4-bit)
+  constexpr int NPT = TILE / kBlock;     // columns per thread in the partial and the final sum
+  constexpr int RB = I4 ? kDn4RB : kDnRB;
+  static_assert(TILE == (I4 ? kTile4 : kTile) && NPT % 2 == 0, "tile shape");
+  static_assert(kBlock * kSeg <= (kBlock / kWave) * TILE, "the id list and the wave sums share one buffer");
+  __shared__ float s_buf[(kBlock / kWave) * TILE];  // the segment's ids, then (after the rows) the four wave sums
   __shared__ int s_red[kBlock / kWave];
   __shared__ int s_last;
   int* s_i = reinterpret_cast<int*>(s_buf);
-  float (*s_acc)[kTile] = reinterpret_cast<float (*)[kTile]>(s_buf);
+  float (*s_acc)[TILE] = reinterpret_cast<float (*)[TILE]>(s_buf);
   constexpr int S = kMaxSplits;
   const int lane = wave_lane(), wv = wave_id();
-  const int col = t * kTile + lane * 8;
+  const int col = t * TILE + lane * CPL;
   const bool colok = col < g.d;
-  const char* wd = reinterpret_cast<const char*>(g.w_dT) + (size_t)col * 2;
+  // fp16: the lane's 16-byte slice of a row; 4-bit: its 8 bytes and the scale of its 128-column group
+  const char* wd = static_cast<const char*>(g.w_dT) + (size_t)col * 2;
   const size_t rb = (size_t)g.d * 2;
-  float acc[8];
+  const uint32_t rowb4 = (uint32_t)g.d / 2, scb4 = (uint32_t)(g.d / 128) * 2;
+  const uint32_t woff4 = colok ? (uint32_t)col / 2 : kOob, soff4 = colok ? (uint32_t)(col / 128) * 2 : kOob;
+  float acc[CPL];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   // candidates: list positions, or the words q = s / 32 + kSW k (bit s % 32)
   int ncand;
   if constexpr (LIST) {
@@ -299,24 +312,54 @@ __device__ __forceinline__ void dn_split(const DnArgs& g, int t, int s) {
     __syncthreads();
     // this wave's ids of the segment: sequence positions base + jj with (base + jj) % 4 == wv
     const int j0 = (wv - (base & 3) + 4) & 3;
-    for (int j = j0; j < ns; j += 4 * kDnRB) {
-      uint4 wr[kDnRB];
-      float av[kDnRB];
+    for (int j = j0; j < ns; j += 4 * RB) {
+      if constexpr (I4) {
+        constexpr int NW = CPL / 8;  // 32-bit words of nibbles per lane and row
+        uint32_t wr[RB][NW];
+        uint32_t sc[RB];
+        float av[RB];
 #pragma unroll
-      for (int r = 0; r < kDnRB; ++r) {
-        const int jj = j + 4 * r;
-        const bool ok = jj < ns;
-        const int i = ok ? s_i[jj] : 0;
-        wr[r] = ldz16(wd + (size_t)i * rb, ok && colok);
-        av[r] = *(ok ? g.a + i : s_zero_f);
-      }
+        for (int r = 0; r < RB; ++r) {
+          const int jj = j + 4 * r;
+          const int i = jj < ns ? s_i[jj] : -1;
+          const __amdgpu_buffer_rsrc_t rr = row_rsrc(g.w_dT, i, rowb4);
+          if constexpr (NW == 2) {
+            const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rr, woff4, 0, 0));
+            wr[r][0] = v.x;
+            wr[r][NW - 1] = v.y;
+          } else {
+            wr[r][0] = __builtin_amdgcn_raw_buffer_load_b32(rr, woff4, 0, 0);
+          }
+          sc[r] = __builtin_amdgcn_raw_buffer_load_b16(row_rsrc(g.s_dT, i, scb4), soff4, 0, 0);
+          av[r] = *(i >= 0 ? g.a + i : s_zero_f);
+        }
 #pragma unroll
-      for (int r = 0; r < kDnRB; ++r) {
-        const uint32_t ww[4] = {wr[r].x, wr[r].y, wr[r].z, wr[r].w};
+        for (int r = 0; r < RB; ++r) {
+          const float f = av[r] * h2f(sc[r]);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          acc[2 * h] = fmaf(av[r], h2f(ww[h] & 0xffffu), acc[2 * h]);
-          acc[2 * h + 1] = fmaf(av[r], h2f(ww[h] >> 16), acc[2 * h + 1]);
+          for (int q = 0; q < NW; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[8 * q + e] = fmaf(f, i4_elem(wr[r][q], e), acc[8 * q + e]);
+        }
+      } else {
+        uint4 wr[RB];
+        float av[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const int jj = j + 4 * r;
+          const bool ok = jj < ns;
+          const int i = ok ? s_i[jj] : 0;
+          wr[r] = ldz16(wd + (size_t)i * rb, ok && colok);
+          av[r] = *(ok ? g.a + i : s_zero_f);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          const uint32_t ww[4] = {wr[r].x, wr[r].y, wr[r].z, wr[r].w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            acc[2 * h] = fmaf(av[r], h2f(ww[h] & 0xffffu), acc[2 * h]);
+            acc[2 * h + 1] = fmaf(av[r], h2f(ww[h] >> 16), acc[2 * h + 1]);
+          }
         }
       }
     }
@@ -325,20 +368,22 @@ __device__ __forceinline__ void dn_split(const DnArgs& g, int t, int s) {
   }
   // the split's partial: the four wave sums in wave order
 #pragma unroll
-  for (int c = 0; c < 8; ++c) s_acc[wv][lane * 8 + c] = acc[c];
+  for (int c = 0; c < CPL; ++c) s_acc[wv][lane * CPL + c] = acc[c];
   __syncthreads();
-  const int c0 = 2 * threadIdx.x;
-  const int gc = t * kTile + c0;  // d % 8 == 0: gc < d implies gc + 1 < d
+  const int c0 = NPT * threadIdx.x;
+  const int gc = t * TILE + c0;  // d % 8 == 0 (fp16), d % 128 == 0 (4-bit): gc < d implies gc + NPT <= d
   if (gc < g.d) {
-    float v0 = s_acc[0][c0], v1 = s_acc[0][c0 + 1];
+    float v[NPT];
 #pragma unroll
-    for (int w = 1; w < kBlock / kWave; ++w) {
-      v0 += s_acc[w][c0];
-      v1 += s_acc[w][c0 + 1];
+    for (int e = 0; e < NPT; ++e) {
+      v[e] = s_acc[0][c0 + e];
+#pragma unroll
+      for (int w = 1; w < kBlock / kWave; ++w) v[e] += s_acc[w][c0 + e];
     }
-    st_dev64(g.part + (size_t)s * g.d + gc, v0, v1);
+#pragma unroll
+    for (int e = 0; e < NPT; e += 2) st_dev64(g.part + (size_t)s * g.d + gc + e, v[e], v[e + 1]);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial store has completed
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t* tk = g.ctr + t * kTicketStride;
@@ -349,26 +394,28 @@ __device__ __forceinline__ void dn_split(const DnArgs& g, int t, int s) {
   __syncthreads();
   if (!s_last || gc >= g.d) return;
   // the tile's last workgroup: y = (y +) (b_down + sum of the S partials in split order)
-  float t0 = g.b_down ? g.b_down[gc] : 0.f, t1 = g.b_down ? g.b_down[gc + 1] : 0.f;
-  constexpr int kFin = 16;  // partials in flight per round
+  float tv[NPT];
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) tv[e] = g.b_down ? g.b_down[gc + e] : 0.f;
+  constexpr int kFin = 16;  // splits per round: 16 NPT / 2 partial pairs in flight
 #pragma unroll
   for (int s0 = 0; s0 < S; s0 += kFin) {
-    uint64_t v[kFin];
+    uint64_t v[kFin][NPT / 2];
 #pragma unroll
-    for (int u = 0; u < kFin; ++u) v[u] = ld_dev64(g.part + (size_t)(s0 + u) * g.d + gc);
+    for (int u = 0; u < kFin; ++u)
 #pragma unroll
-    for (int u = 0; u < kFin; ++u) {
-      t0 += __uint_as_float((uint32_t)v[u]);
-      t1 += __uint_as_float((uint32_t)(v[u] >> 32));
-    }
+      for (int e = 0; e < NPT / 2; ++e) v[u][e] = ld_dev64(g.part + (size_t)(s0 + u) * g.d + gc + 2 * e);
+#pragma unroll
+    for (int u = 0; u < kFin; ++u)
+#pragma unroll
+      for (int e = 0; e < NPT / 2; ++e) {
+        tv[2 * e] += __uint_as_float((uint32_t)v[u][e]);
+        tv[2 * e + 1] += __uint_as_float((uint32_t)(v[u][e] >> 32));
+      }
   }
   float* yp = g.y + gc;
-  if (g.accumulate) {
-    t0 = yp[0] + t0;
-    t1 = yp[1] + t1;
-  }
-  yp[0] = t0;
-  yp[1] = t1;
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) yp[e] = g.accumulate ? yp[e] + tv[e] : tv[e];
 }
 
 // k_dn: the down projection, workgroup (t, s) = blockIdx % T, blockIdx / T; in mask mode one more
@@ -380,14 +427,14 @@ struct DnList {
   int32_t* count;
 };
 
-template <bool LIST>
+template <bool LIST, bool I4>
 __global__ __launch_bounds__(kBlock) void k_dn(DnArgs g, DnList out) {
   const int b = blockIdx.x;
   if (!LIST && b == g.T * kMaxSplits) {
     write_list(g.masks, g.nq, out.idx, out.count);
     return;
   }
-  dn_split<LIST>(g, b % g.T, b / g.T);
+  dn_split<LIST, I4>(g, b % g.T, b / g.T);
 }
 
 // the ascending list of kept neurons and its length from the mask words, in rounds of kBlock * kLW
@@ -420,6 +467,138 @@ __device__ __forceinline__ void write_list(const uint32_t* masks, int nq, int32_
     __syncthreads();  // s_red is rewritten by the next round
   }
   if (threadIdx.x == 0) *count = base;
+}
+
+// =========================================================================================
+// 4-bit weights at one token (ReLU): the same pipeline as fp16 (k_qu's up rows and k_up1_i4 share
+// the 4-bit up-row code; k_dn<., true> takes 16 columns, 8 bytes, of each row per lane).  Row i of
+// W_up and of W_dT holds d/2 bytes (element 2j in the low nibble of byte j, two's complement) and
+// d/128 fp16 scales, one per 128 consecutive elements.
+
+
+struct Up4Args {
+  const int32_t* idx;
+  const int32_t* count;
+  const uint8_t* w_up;
+  const uint16_t* s_up;
+  const float* b_up;
+  const _Float16* x;
+  float* a;
+  uint32_t* ctr;
+  int F, d, T;
+};
+
+// The 4-bit up rows in k_up1's scheme with 32-element slices: wave w covers the quarter
+// [w S4, w S4 + S4) of a row's slices and lane L its slices w S4 + L + 64 u (u < kUQ4).  A slice
+// lies in one scale group, so its dot product (exact fp16 products, fp32 sums) takes one scale;
+// the row's value is then committed as in up_rows_finish.  The lane's x slices are loaded and
+// paired (pair_x8) once per workgroup.
+struct Up4Slices {
+  uint32_t woff[kUQ4], xoff[kUQ4], soff[kUQ4];  // byte offsets in a weight row, x, a scale row (kOob: none)
+};
+
+__device__ __forceinline__ Up4Slices up4_slices(int d) {
+  const int nsl = d / 32, S4 = (nsl + 3) / 4;
+  const int w = wave_id(), L = wave_lane();
+  Up4Slices o;
+#pragma unroll
+  for (int u = 0; u < kUQ4; ++u) {
+    const int k = L + kWave * u, sl = w * S4 + k;
+    const bool ok = k < S4 && sl < nsl;
+    o.woff[u] = ok ? (uint32_t)sl * 16 : kOob;
+    o.xoff[u] = ok ? (uint32_t)sl * 64 : kOob;
+    o.soff[u] = ok ? (uint32_t)(sl / 4) * 2 : kOob;
+  }
+  return o;
+}
+
+__device__ __forceinline__ void x4_slices(const _Float16* __restrict__ x, int d, const Up4Slices& o,
+                                          uint4 (&px)[kUQ4][4]) {
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(x), 0, d * 2, kRsrcWord3);
+#pragma unroll
+  for (int u = 0; u < kUQ4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) px[u][v] = bload16(xr, o.xoff[u] == kOob ? kOob : o.xoff[u] + 16 * v);
+#pragma unroll
+  for (int u = 0; u < kUQ4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) px[u][v] = pair_x8(px[u][v]);
+}
+
+__device__ __forceinline__ void up4_rows_load(const uint8_t* __restrict__ w_up, const uint16_t* __restrict__ s_up,
+                                              int d, const int (&ids)[kRPG], const Up4Slices& o,
+                                              uint4 (&wq)[kRPG][kUQ4], uint32_t (&sc)[kRPG][kUQ4]) {
+  const uint32_t rowb = (uint32_t)d / 2, scb = (uint32_t)(d / 128) * 2;
+#pragma unroll
+  for (int r = 0; r < kRPG; ++r) {
+    const __amdgpu_buffer_rsrc_t wr = row_rsrc(w_up, ids[r], rowb);
+    const __amdgpu_buffer_rsrc_t sr = row_rsrc(s_up, ids[r], scb);
+#pragma unroll
+    for (int u = 0; u < kUQ4; ++u) {
+      wq[r][u] = bload16(wr, o.woff[u]);
+      sc[r][u] = __builtin_amdgcn_raw_buffer_load_b16(sr, o.soff[u], 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void up4_rows_finish(const uint4 (&wq)[kRPG][kUQ4], const uint32_t (&sc)[kRPG][kUQ4],
+                                                const uint4 (&px)[kUQ4][4], const int (&ids)[kRPG],
+                                                const float* __restrict__ b_up, float* __restrict__ a, float* s_p) {
+  const int lane = wave_lane(), wv = wave_id();
+#pragma unroll
+  for (int r = 0; r < kRPG; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < kUQ4; ++u) {
+      float t = 0.f;
+      t = dot8_i4(wq[r][u].x, px[u][0], t);
+      t = dot8_i4(wq[r][u].y, px[u][1], t);
+      t = dot8_i4(wq[r][u].z, px[u][2], t);
+      t = dot8_i4(wq[r][u].w, px[u][3], t);
+      acc = fmaf(t, h2f(sc[r][u]), acc);
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) s_p[r * 4 + wv] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < kRPG) {
+    const int r = threadIdx.x;
+    int i = -1;
+#pragma unroll
+    for (int k = 0; k < kRPG; ++k)
+      if (k == r) i = ids[k];
+    if (i >= 0) {
+      const float z = ((s_p[r * 4] + s_p[r * 4 + 1]) + s_p[r * 4 + 2]) + s_p[r * 4 + 3];
+      const float v = z + (b_up ? b_up[i] : 0.f);
+      a[i] = v > 0.f ? v : 0.f;
+    }
+  }
+  __syncthreads();
+}
+
+// k_up1_i4: a_i for the neurons of a given list with 4-bit rows (FFN call), kRPG list entries per
+// workgroup at a time; entries outside [0, F) are skipped.  Workgroup 0 zeroes k_dn's tickets.
+__global__ __launch_bounds__(kBlock) void k_up1_i4(Up4Args g) {
+  __shared__ float s_p[kRPG * 4];
+  if (blockIdx.x == 0) zero_tickets(g.ctr, g.T);
+  int n = *g.count;
+  n = n < 0 ? 0 : (n > g.F ? g.F : n);
+  if ((int)blockIdx.x * kRPG >= n) return;  // (uniform)
+  const Up4Slices o = up4_slices(g.d);
+  uint4 px[kUQ4][4];
+  x4_slices(g.x, g.d, o, px);
+  for (int k0 = blockIdx.x * kRPG; k0 < n; k0 += gridDim.x * kRPG) {
+    int ids[kRPG];
+#pragma unroll
+    for (int r = 0; r < kRPG; ++r) {
+      const int v = k0 + r < n ? __builtin_amdgcn_readfirstlane(g.idx[k0 + r]) : -1;
+      ids[r] = (unsigned)v < (unsigned)g.F ? v : -1;
+    }
+    uint4 wq[kRPG][kUQ4];
+    uint32_t sc[kRPG][kUQ4];
+    up4_rows_load(g.w_up, g.s_up, g.d, ids, o, wq, sc);
+    up4_rows_finish(wq, sc, px, ids, g.b_up, g.a, s_p);
+  }
 }
 
 // =========================================================================================
@@ -461,7 +640,8 @@ struct QuArgs {
   const float* h;
   float* logits;
   uint32_t* masks;
-  const _Float16* w_up;
+  const void* w_up;      // fp16 rows of d, or 4-bit rows of d/2 bytes
+  const uint16_t* s_up;  // 4-bit: fp16 scales [F][d/128]
   const float* b_up;  // or null
   const _Float16* x;
   float* a;           // [F] activations by neuron
@@ -470,7 +650,7 @@ struct QuArgs {
   float thr;
 };
 
-template <int RV>
+template <int RV, bool I4>
 __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   const int q = blockIdx.x;
   if (q == 0) zero_tickets(g.ctr, g.T);
@@ -484,15 +664,31 @@ __global__ __launch_bounds__(kBlock) void k_qu(QuArgs g) {
   __shared__ float s_p[kRPG * 4];
   const uint32_t mu = __builtin_amdgcn_readfirstlane(m);
   const int nset = __popc(mu);
-  const UpSlices o = up_slices(g.d);
-  uint4 xv[kUQ], w[kRPG][kUQ];
-  x_slices(g.x, g.d, o, xv);
-  for (int j0 = 0; j0 < nset; j0 += kRPG) {
-    int ids[kRPG];
+  if constexpr (I4) {
+    const Up4Slices o = up4_slices(g.d);
+    uint4 px[kUQ4][4], wq[kRPG][kUQ4];
+    uint32_t sc[kRPG][kUQ4];
+    x4_slices(g.x, g.d, o, px);
+    for (int j0 = 0; j0 < nset; j0 += kRPG) {
+      int ids[kRPG];
 #pragma unroll
-    for (int r = 0; r < kRPG; ++r) ids[r] = j0 + r < nset ? chunk_neuron<kIlv, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
-    up_rows_load(g.w_up, g.d, ids, o, w);
-    up_rows_finish(w, xv, ids, g.b_up, g.a, s_p);
+      for (int r = 0; r < kRPG; ++r)
+        ids[r] = j0 + r < nset ? chunk_neuron<kIlv, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
+      up4_rows_load(static_cast<const uint8_t*>(g.w_up), g.s_up, g.d, ids, o, wq, sc);
+      up4_rows_finish(wq, sc, px, ids, g.b_up, g.a, s_p);
+    }
+  } else {
+    const UpSlices o = up_slices(g.d);
+    uint4 xv[kUQ], w[kRPG][kUQ];
+    x_slices(g.x, g.d, o, xv);
+    for (int j0 = 0; j0 < nset; j0 += kRPG) {
+      int ids[kRPG];
+#pragma unroll
+      for (int r = 0; r < kRPG; ++r)
+        ids[r] = j0 + r < nset ? chunk_neuron<kIlv, 4>(q, g.NC, nth_bit(mu, j0 + r)) : -1;
+      up_rows_load(static_cast<const _Float16*>(g.w_up), g.d, ids, o, w);
+      up_rows_finish(w, xv, ids, g.b_up, g.a, s_p);
+    }
   }
 }
 
@@ -522,9 +718,13 @@ StreamBufs stream_bufs(void* ws, int F, int d) {
 }
 
 template <int RV>
-void qu_launch(const QuArgs& g, hipStream_t s) {
-  k_qu<RV><<<g.NC, kBlock, 0, s>>>(g);
+void qu_launch(const QuArgs& g, bool i4, hipStream_t s) {
+  if (i4) k_qu<RV, true><<<g.NC, kBlock, 0, s>>>(g);
+  else k_qu<RV, false><<<g.NC, kBlock, 0, s>>>(g);
 }
+
+// the down projection's column tiles (and ticket lines): kTile columns for fp16 rows, kTile4 for 4-bit
+int dn_tiles(const psffn_ffn& W) { return W.dt == PSFFN_I4G128 ? (W.d + kTile4 - 1) / kTile4 : tiles_of(W.d); }
 
 }  // namespace
 
@@ -537,8 +737,13 @@ bool stream_ffn_fits(const psffn_ffn& W, int B) {
   return B == 1 && W.dt == PSFFN_F16 && W.act == PSFFN_RELU && W.d % 8 == 0 && W.d <= kUQ * 4 * kWave * 8;
 }
 
+bool stream_ffn_i4_fits(const psffn_ffn& W, int B) {
+  return B == 1 && W.dt == PSFFN_I4G128 && W.act == PSFFN_RELU && W.d % 128 == 0 && W.d <= kUQ4 * 4 * kWave * 32;
+}
+
 bool stream_layer_fits(const psffn_predictor& P, const psffn_ffn& W, int B, bool ln) {
-  if (!stream_ffn_fits(W, B) || P.dt != PSFFN_F16 || P.F != W.F || P.d != W.d) return false;
+  if (!(stream_ffn_fits(W, B) || stream_ffn_i4_fits(W, B)) || P.dt != PSFFN_F16 || P.F != W.F || P.d != W.d)
+    return false;
   const int rv = (P.r + kWave * 8 - 1) / (kWave * 8);
   if (rv < 1 || rv > 4 || (W.F + 31) / 32 > kMaxWords) return false;
   if (ln && ln_k(P.d) == 0) return false;
@@ -547,6 +752,39 @@ bool stream_layer_fits(const psffn_predictor& P, const psffn_ffn& W, int B, bool
 
 hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* idx, const int32_t* count, float* y,
                              int accumulate, void* ws, hipStream_t s) {
+  if (stream_ffn_i4_fits(W, 1)) {
+    const StreamBufs bf = stream_bufs(ws, W.F, W.d);
+    Up4Args u{};
+    u.idx = idx;
+    u.count = count;
+    u.w_up = static_cast<const uint8_t*>(W.w_up);
+    u.s_up = static_cast<const uint16_t*>(W.s_up);
+    u.b_up = W.b_up;
+    u.x = static_cast<const _Float16*>(x);
+    u.a = bf.a;
+    u.ctr = bf.ctr;
+    u.F = W.F;
+    u.d = W.d;
+    u.T = dn_tiles(W);
+    const int grid = W.F < kRPG * 1024 ? (W.F + kRPG - 1) / kRPG : 1024;
+    k_up1_i4<<<grid, kBlock, 0, s>>>(u);
+    DnArgs g{};
+    g.idx = idx;
+    g.count = count;
+    g.a = bf.a;
+    g.w_dT = W.w_dT;
+    g.s_dT = static_cast<const uint16_t*>(W.s_dT);
+    g.b_down = W.b_down;
+    g.part = bf.part;
+    g.ctr = bf.ctr;
+    g.y = y;
+    g.d = W.d;
+    g.F = W.F;
+    g.T = dn_tiles(W);
+    g.accumulate = accumulate;
+    k_dn<true, true><<<(unsigned)(g.T * kMaxSplits), kBlock, 0, s>>>(g, DnList{});
+    return hipGetLastError();
+  }
   if (!stream_ffn_fits(W, 1)) return hipErrorNotSupported;
   const StreamBufs bf = stream_bufs(ws, W.F, W.d);
   UpArgs u{};
@@ -566,7 +804,7 @@ hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* i
   g.idx = idx;
   g.count = count;
   g.a = bf.a;
-  g.w_dT = static_cast<const _Float16*>(W.w_dT);
+  g.w_dT = W.w_dT;
   g.b_down = W.b_down;
   g.part = bf.part;
   g.ctr = bf.ctr;
@@ -575,7 +813,7 @@ hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* i
   g.F = W.F;
   g.T = tiles_of(W.d);
   g.accumulate = accumulate;
-  k_dn<true><<<(unsigned)(g.T * kMaxSplits), kBlock, 0, s>>>(g, DnList{});
+  k_dn<true, false><<<(unsigned)(g.T * kMaxSplits), kBlock, 0, s>>>(g, DnList{});
   return hipGetLastError();
 }
 
@@ -586,10 +824,15 @@ hipError_t launch_layer_stream(const psffn_predictor& P, const psffn_ffn& W, con
   const StreamBufs bf = stream_bufs(ws, W.F, W.d);
   uint32_t* masks = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + state_layout(P.F).masks);
   const int nq = (P.F + 31) / 32;
-  // the first kernel zeroes the mask words (k_qu ORs its bits into them)
-  if (ln.xres == nullptr) {
+  const bool i4 = W.dt == PSFFN_I4G128;
+  // the first kernel zeroes the mask words (k_qu ORs its bits into them); k_h1 holds rows of up to
+  // 24 * 512 elements, longer rows (4-bit layers, d <= 16384) and the LayerNorm take k_h
+  if (ln.xres == nullptr && P.d <= kUQ * 4 * kWave * 8) {
     k_h1<kUQ * 4><<<P.r, kWave, 0, s>>>(static_cast<const _Float16*>(P.A), static_cast<const _Float16*>(x), P.d, bf.h,
                                          masks, nq);
+  } else if (ln.xres == nullptr && P.d <= 24 * kWave * 8) {
+    k_h1<24><<<P.r, kWave, 0, s>>>(static_cast<const _Float16*>(P.A), static_cast<const _Float16*>(x), P.d, bf.h,
+                                   masks, nq);
   } else {
     const hipError_t e = launch_h_f16_b1(P, x, bf.h, ln, s, masks, nq, nullptr, 0);
     if (e != hipSuccess) return e;
@@ -600,12 +843,13 @@ hipError_t launch_layer_stream(const psffn_predictor& P, const psffn_ffn& W, con
   q.h = bf.h;
   q.logits = logits;
   q.masks = masks;
-  q.w_up = static_cast<const _Float16*>(W.w_up);
+  q.w_up = W.w_up;
+  q.s_up = static_cast<const uint16_t*>(W.s_up);
   q.b_up = W.b_up;
   q.x = static_cast<const _Float16*>(ln.xres ? static_cast<const void*>(ln.hout) : x);
   q.a = bf.a;
   q.ctr = bf.ctr;
-  q.T = tiles_of(W.d);
+  q.T = dn_tiles(W);
   q.r = P.r;
   q.F = P.F;
   q.d = P.d;
@@ -613,24 +857,26 @@ hipError_t launch_layer_stream(const psffn_predictor& P, const psffn_ffn& W, con
   q.n_hot = n_hot;
   q.thr = thr;
   const int rv = (P.r + kWave * 8 - 1) / (kWave * 8);
-  if (rv == 1) qu_launch<1>(q, s);
-  else if (rv == 2) qu_launch<2>(q, s);
-  else if (rv == 3) qu_launch<3>(q, s);
-  else qu_launch<4>(q, s);
+  if (rv == 1) qu_launch<1>(q, i4, s);
+  else if (rv == 2) qu_launch<2>(q, i4, s);
+  else if (rv == 3) qu_launch<3>(q, i4, s);
+  else qu_launch<4>(q, i4, s);
   DnArgs g{};
   g.masks = masks;
   g.nq = nq;
   g.a = bf.a;
-  g.w_dT = static_cast<const _Float16*>(W.w_dT);
+  g.w_dT = W.w_dT;
+  g.s_dT = static_cast<const uint16_t*>(W.s_dT);
   g.b_down = W.b_down;
   g.part = bf.part;
   g.ctr = bf.ctr;
   g.y = ln.xres ? const_cast<float*>(ln.xres) : y;
   g.d = W.d;
   g.F = W.F;
-  g.T = tiles_of(W.d);
+  g.T = dn_tiles(W);
   g.accumulate = ln.xres ? 1 : accumulate;
-  k_dn<false><<<(unsigned)(g.T * kMaxSplits + 1), kBlock, 0, s>>>(g, DnList{idx, count});
+  if (i4) k_dn<false, true><<<(unsigned)(g.T * kMaxSplits + 1), kBlock, 0, s>>>(g, DnList{idx, count});
+  else k_dn<false, false><<<(unsigned)(g.T * kMaxSplits + 1), kBlock, 0, s>>>(g, DnList{idx, count});
   return hipGetLastError();
 }
 

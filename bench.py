@@ -359,6 +359,8 @@ def layer_kernels(spec, B):
     kernels otherwise)."""
     if B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
         return "k_h1, k_qu, k_dn"
+    if B == 1 and spec.storage == "i4" and spec.act == "relu" and spec.d <= 16384:
+        return ("k_h1, " if spec.d <= 12288 else "k_h, ") + "k_qu (4-bit up rows), k_dn (4-bit rows)"
     if B == 1 or spec.storage == "f32":
         return "k_h, k_q, k_ud, k_reduce_ud"
     return "small-batch or MFMA batch kernels by batch size"

@@ -142,7 +142,7 @@ psffn_status psffn_sparse_ffn(const psffn_ffn* W, const void* x, int B, const in
 
 /* One decode step of one layer: psffn_predict followed by psffn_sparse_ffn on its list, with
  * the same outputs (idx ascending, count, optional logits, y, bit for bit) and the same
- * requirements, in the fewest launches: at one token with fp16 ReLU weights the up rows are
+ * requirements, in the fewest launches: at one token with fp16 or 4-bit ReLU weights the up rows are
  * computed inside the predictor's logits kernel and the list is written by the down projection;
  * elsewhere the list is ordered inside the FFN's first kernel instead of by the predictor.
  * P and W must describe the same layer (same F and d); P->dt is fp32 exactly when W->dt is fp32. */
