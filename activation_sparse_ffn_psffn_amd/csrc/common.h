@@ -249,7 +249,9 @@ hipError_t launch_h_f16_b1(const psffn_predictor& P, const void* x, float* h, co
 // words: stream_scratch bytes.  NotSupported outside the shapes the *_fits calls accept.
 size_t stream_scratch(int r, int F, int d);
 bool stream_ffn_fits(const psffn_ffn& W, int B);
-bool stream_ffn_i4_fits(const psffn_ffn& W, int B);  // one token, 4-bit ReLU weights: k_up1_i4 + k_dn_i4
+bool stream_ffn_i4_fits(const psffn_ffn& W, int B);
+// h = A x at one token by k_h1 (fp16 predictor, rows of A up to 12288): the bits of k_h
+hipError_t launch_h1(const psffn_predictor& P, const void* x, float* h, hipStream_t s);  // one token, 4-bit ReLU weights: k_up1_i4 + k_dn_i4
 bool stream_layer_fits(const psffn_predictor& P, const psffn_ffn& W, int B, bool ln);
 hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* idx, const int32_t* count, float* y,
                              int accumulate, void* ws, hipStream_t s);

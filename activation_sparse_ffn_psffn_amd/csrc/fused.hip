@@ -931,8 +931,12 @@ static hipError_t predict_t(const psffn_predictor& P, const void* x, int B, floa
   uint32_t* masks = reinterpret_cast<uint32_t*>(w + L.masks);
   float* h = reinterpret_cast<float*>(w + L.scratch);
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
-  k_h<PT, NB, 0><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h,
-                                                                                             0.f, nullptr);
+  // one token, fp16: k_h1 (one single-wave workgroup per row of A, the same h bits as k_h)
+  const hipError_t eh = PT == St::F16 && B == 1 ? launch_h1(P, x, h, s) : hipErrorNotSupported;
+  if (eh != hipSuccess && eh != hipErrorNotSupported) return eh;
+  if (eh == hipErrorNotSupported)
+    k_h<PT, NB, 0><<<(P.r + kHThreads / kWave - 1) / (kHThreads / kWave), kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B,
+                                                                                               h, 0.f, nullptr);
   k_q<PT, NB, RV, RPW><<<NC, kBlock, 0, s>>>(P.Q, P.c, h, P.r, P.F, thr, B, logits, NC, masks, n_hot);
   k_list<<<1, kListThreads, 4 * (size_t)NQ, s>>>(masks, NQ, P.F, idx, count);
   return hipGetLastError();

@@ -733,6 +733,15 @@ size_t stream_scratch(int r, int F, int d) {
          round256((size_t)r * 4);
 }
 
+hipError_t launch_h1(const psffn_predictor& P, const void* x, float* h, hipStream_t s) {
+  if (P.dt != PSFFN_F16 || P.d > 24 * kWave * 8) return hipErrorNotSupported;
+  const _Float16* A = static_cast<const _Float16*>(P.A);
+  const _Float16* xv = static_cast<const _Float16*>(x);
+  if (P.d <= kUQ * 4 * kWave * 8) k_h1<kUQ * 4><<<P.r, kWave, 0, s>>>(A, xv, P.d, h, nullptr, 0);
+  else k_h1<24><<<P.r, kWave, 0, s>>>(A, xv, P.d, h, nullptr, 0);
+  return hipGetLastError();
+}
+
 bool stream_ffn_fits(const psffn_ffn& W, int B) {
   return B == 1 && W.dt == PSFFN_F16 && W.act == PSFFN_RELU && W.d % 8 == 0 && W.d <= kUQ * 4 * kWave * 8;
 }
