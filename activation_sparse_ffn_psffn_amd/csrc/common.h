@@ -244,14 +244,14 @@ hipError_t launch_layer_fused(const psffn_predictor& P, const psffn_ffn& W, cons
 hipError_t launch_h_f16_b1(const psffn_predictor& P, const void* x, float* h, const LnArgs& ln, hipStream_t s,
                            uint32_t* zero, int nzero, uint32_t* zero2, int nzero2);
 
-// streamed one-token pipeline (stream.hip; fp16 predictor, fp16 ReLU weights): the up rows ride on
-// the logits kernel, the down projection sums its split partials itself.  Scratch after the mask
-// words: stream_scratch bytes.  NotSupported outside the shapes the *_fits calls accept.
+// streamed one-token pipeline (stream.hip; fp16 predictor, fp16 or 4-bit ReLU weights): the up rows
+// ride on the logits kernel, the down projection sums its split partials itself.  Scratch after the
+// mask words: stream_scratch bytes.  NotSupported outside the shapes the *_fits calls accept.
 size_t stream_scratch(int r, int F, int d);
-bool stream_ffn_fits(const psffn_ffn& W, int B);
-bool stream_ffn_i4_fits(const psffn_ffn& W, int B);
+bool stream_ffn_fits(const psffn_ffn& W, int B);     // one token, fp16 ReLU weights: k_up1 + k_dn
+bool stream_ffn_i4_fits(const psffn_ffn& W, int B);  // one token, 4-bit ReLU weights: k_up1_i4 + k_dn
 // h = A x at one token by k_h1 (fp16 predictor, rows of A up to 12288): the bits of k_h
-hipError_t launch_h1(const psffn_predictor& P, const void* x, float* h, hipStream_t s);  // one token, 4-bit ReLU weights: k_up1_i4 + k_dn_i4
+hipError_t launch_h1(const psffn_predictor& P, const void* x, float* h, hipStream_t s);
 bool stream_layer_fits(const psffn_predictor& P, const psffn_ffn& W, int B, bool ln);
 hipError_t launch_ffn_stream(const psffn_ffn& W, const void* x, const int32_t* idx, const int32_t* count, float* y,
                              int accumulate, void* ws, hipStream_t s);
