@@ -45,3 +45,23 @@ def test_hot_prefix_len_from_profile_counts():
         bench.hot_prefix_len(torch.tensor([1, 9], dtype=torch.int32), 10, 0.5)  # not hot-first
     with pytest.raises(ValueError):
         bench.hot_prefix_len(counts, 512, 0.0)
+
+
+def test_traffic_hash_ignores_comments_only(tmp_path, monkeypatch):
+    # the traffic figures stay valid across comment edits and are dropped by any code edit
+    code = "int f(int x) { return x + 1; }\n"
+    for f in bench.TRAFFIC_SOURCES:
+        p = tmp_path / f
+        p.parent.mkdir(parents=True, exist_ok=True)
+        p.write_text(code)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.sources_hash()
+    first = tmp_path / bench.TRAFFIC_SOURCES[0]
+    first.write_text("// a comment\nint f(int x) {  /* another */ return x + 1; }\n")
+    assert bench.sources_hash() == h0
+    first.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.sources_hash() != h0
+    monkeypatch.setattr(bench, "TRAFFIC", {("w", 1): {"sources": h0, "bytes": 7}})
+    assert bench.measured_traffic("w", 1) is None
+    first.write_text(code)
+    assert bench.measured_traffic("w", 1) == 7
