@@ -361,10 +361,16 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def layer_kernels(spec, B):
-    """The kernels one psffn_layer call launches for this workload and batch (as the library picks
-    its pipeline: small-batch kernels at one token and for the shapes they take, MFMA batch
-    kernels otherwise)."""
+def layer_kernels(spec, B, ln=False):
+    """The kernels one psffn_layer (ln: psffn_layer_ln) call launches for this workload and batch (as
+    the library picks its pipeline: small-batch kernels at one token and for the shapes they take,
+    MFMA batch kernels otherwise)."""
+    if ln and B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
+        return "k_h with the LayerNorm, k_qu, k_dn"
+    if ln and B == 2 and spec.storage == "f16" and spec.act == "relu" and spec.r <= 1024:
+        return "k_h with the LayerNorm, k_q, k_ud, k_reduce_ud"
+    if ln and B > 1:
+        return "the LayerNorm kernel, then the small-batch or batch kernels by batch size"
     if B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
         return "k_h1, k_qu, k_dn"
     if B == 1 and spec.storage == "i4" and spec.act == "relu" and spec.d <= 16384:
@@ -430,7 +436,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
     gbps = byt / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-            "kernel": "psffn_layer_ln (%s), 48 calls per step" % layer_kernels(spec, B),
+            "kernel": "psffn_layer_ln (%s), 48 calls per step" % layer_kernels(spec, B, ln=True),
             "bytes_per_launch": int(byt / L), "avg_launch_us": round(ms * 1e3 / L, 3)}
     cpu = None
     if not args.no_cpu_baseline:
