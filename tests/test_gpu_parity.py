@@ -494,3 +494,33 @@ def test_widest_rows(d, B):
     _, _, h2 = ps.layer_ln(P, W, x2, ws)
     torch.cuda.synchronize()
     assert torch.equal(h1, h2) and torch.equal(x1, x2)
+
+
+@pytest.mark.parametrize("d,F", [(12288, 400), (16384, 400), (16512, 400), (128, 262144)])
+def test_4bit_one_token_limits(d, F):
+    # the one-token pipeline with 4-bit rows: h by k_h1 up to d = 12288 and by k_h above; 4-bit up
+    # rows of at most 16384 elements (two 32-element slices per lane); one row more and the small-batch
+    # kernels take over; F = 262144: the most neurons (8192 mask words) with one 512-column tile
+    spec = spec_variant("opt175b_relu_i4", density=0.05)
+    say("4-bit one token d", d, "F", F)
+    L = synth.make_layer(spec, seed=7, device=DEV, d=d, F=F, r=24)
+    n = L.numpy()
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, 1)
+    X = synth.make_tokens(L.spec, 1, seed=8, device=DEV, d=d)
+    Xn = X.cpu().numpy()
+    idx, cnt = ps.predict(P, X, ws)
+    y1 = ps.sparse_ffn(W, X, idx, cnt, ws)
+    idx2, cnt2, y2 = ps.layer(P, W, X, ws)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    st = check_set(idx, cnt, ref)
+    m = int(cnt.item())
+    assert int(cnt2.item()) == m and torch.equal(idx2[:m], idx[:m]) and torch.equal(y1, y2)
+    lst = oracle.compact(ref)
+    orc = oracle_layer(n, "relu")
+    y_o = ps.sparse_ffn(W, X, torch.from_numpy(lst).to(DEV), torch.tensor([len(lst)], dtype=torch.int32,
+                                                                          device=DEV), ws)
+    check_y(y_o.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("i4"))
+    if st["exact"]:
+        check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for("i4"))
