@@ -1,22 +1,24 @@
-// Streamed one-token pipeline for fp16 predictors and fp16 ReLU weights.
+// Streamed one-token pipeline for fp16 predictors and fp16 or 4-bit (g128) ReLU weights.
 //
 // Layer call, three kernels:
-//   k_h    h = A x (the small-batch pipeline's kernel; with the stack step's LayerNorm inside)
+//   k_h1   h = A x, one single-wave workgroup per row of A (the bits of the small-batch k_h, which
+//          takes over for rows longer than 12288 and for the stack step's LayerNorm)
 //   k_qu   per chunk of 16 neurons: l = Q h + c, the threshold test and the chunk's mask bits, and
 //          then, in the same workgroup, the up rows of the chunk's kept neurons,
 //          a_i = max(W_up[i] . x + b_up[i], 0).  The up rows stream while other workgroups still
 //          stream Q, instead of after the whole predictor.
 //   k_dn   the down projection, y = b_down + sum_i a_i W_dT[i], by (column tile, split): split s
 //          takes the kept neurons i with i mod S == s (in a hot-first layer the hot neurons are
-//          low-indexed, so this spreads them evenly), column tile t takes 512 output columns (one
-//          1 KB segment of every fp16 row).  Each workgroup writes its tile's partial sum; the last
-//          of a tile's S workgroups to finish (a completion count per tile, no spin-wait) adds the
-//          S partials in split order and writes y.  Workgroup 0 writes the ascending list of kept
-//          neurons and its length.
-// FFN call on a given list: k_up1 (the up rows of the listed neurons, one wave per row, the same
-// arithmetic as k_qu) and k_dn in list mode (split s takes the list entries with i mod S == s, in
-// list order).  On the ascending list of a predictor call that is the same sequence as the layer
-// call's, so psffn_layer equals psffn_predict followed by psffn_sparse_ffn bit for bit.
+//          low-indexed, so this spreads them evenly), column tile t takes 512 output columns (1 KB
+//          of every fp16 row, 256 bytes of every 4-bit row).  Each workgroup writes its tile's
+//          partial sum; the last of a tile's S workgroups to finish (a completion count per tile,
+//          no spin-wait) adds the S partials in split order and writes y.  One more workgroup
+//          writes the ascending list of kept neurons and its length.
+// FFN call on a given list: k_up1 / k_up1_i4 (the up rows of the listed neurons, two at a time by
+// a whole workgroup, the same arithmetic as k_qu) and k_dn in list mode (split s takes the list
+// entries with i mod S == s, in list order).  On the ascending list of a predictor call that is the
+// same sequence as the layer call's, so psffn_layer equals psffn_predict followed by
+// psffn_sparse_ffn bit for bit.
 //
 // Method ("PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU", Elamur
 // Research summary): Summary 2nd paragraph (a per-layer predictor guesses the firing neurons;
