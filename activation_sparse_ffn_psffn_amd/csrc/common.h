@@ -146,17 +146,22 @@ __device__ __forceinline__ float block_sum(float v, float* s_red) {
 // Two block reductions (mean, then the centred sum of squares), then out[j] = 4 halves (uint2;
 // global or LDS).  The LayerNorm kernel and the layer call's first kernel both use it, so they give
 // the same bits.
+// The row's loads (ln_row_load) and the rest (ln_row_finish) are separate so that a caller can
+// issue the loads early; ln_row_f16 is the two in a row.
 template <int K>
-__device__ __forceinline__ void ln_row_f16(const float* __restrict__ xrow, int d, float eps, float* s_red,
-                                           uint2* out) {
+__device__ __forceinline__ void ln_row_load(const float* __restrict__ xrow, int d, float4 (&v)[K]) {
   const float4* xr = reinterpret_cast<const float4*>(xrow);
   const int n4 = d / 4;
-  float4 v[K];
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int j = threadIdx.x + k * kBlock;
     v[k] = j < n4 ? xr[j] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+}
+
+template <int K>
+__device__ __forceinline__ void ln_row_finish(const float4 (&v)[K], int d, float eps, float* s_red, uint2* out) {
+  const int n4 = d / 4;
   float sm = 0.f;
 #pragma unroll
   for (int k = 0; k < K; ++k) sm += (v[k].x + v[k].y) + (v[k].z + v[k].w);
@@ -183,6 +188,14 @@ __device__ __forceinline__ void ln_row_f16(const float* __restrict__ xrow, int d
       out[j] = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     }
   }
+}
+
+template <int K>
+__device__ __forceinline__ void ln_row_f16(const float* __restrict__ xrow, int d, float eps, float* s_red,
+                                           uint2* out) {
+  float4 v[K];
+  ln_row_load<K>(xrow, d, v);
+  ln_row_finish<K>(v, d, eps, s_red, out);
 }
 
 // float4 per thread that ln_row_f16 needs for a row of d (1, 2, 4, 8 or 16; 0 above 16384)

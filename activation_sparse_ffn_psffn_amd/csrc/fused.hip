@@ -86,7 +86,12 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
   for (int k = blockIdx.x * kHThreads + threadIdx.x; k < nzero; k += gridDim.x * kHThreads) zero[k] = 0u;
   for (int k = blockIdx.x * kHThreads + threadIdx.x; k < nzero2; k += gridDim.x * kHThreads) zero2[k] = 0u;
   const char* arow = reinterpret_cast<const char*>(A) + (size_t)(j < r ? j : 0) * d * ESZ;
-  // this wave's row loads go out first, then the workgroup stages x (all tokens) in LDS
+  // one token with the LayerNorm: the residual row's loads go out first, so that the LayerNorm's
+  // reductions run while this wave's row of A is still in flight (loads return in issue order)
+  static_assert(LNK == 0 || kHThreads == kBlock, "ln_row_* take kBlock threads");
+  float4 xln[(LNK > 0 && NB == 1) ? LNK : 1];
+  if constexpr (LNK > 0 && NB == 1) ln_row_load<LNK>(reinterpret_cast<const float*>(x), d, xln);
+  // this wave's row loads, then the workgroup stages x (all tokens) in LDS
   uint4 w[UN];
   int base = lane * EPL;
 #pragma unroll
@@ -97,9 +102,13 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
   if constexpr (LNK > 0) {
     static_assert(PT == St::F16, "the LayerNorm output is fp16");
     __shared__ float s_red[kHThreads / kWave];
-    for (int b = 0; b < nb; ++b)
-      ln_row_f16<LNK>(reinterpret_cast<const float*>(x) + (size_t)b * d, d, eps, s_red,
-                      reinterpret_cast<uint2*>(s_x) + (size_t)b * d / 4);
+    if constexpr (NB == 1) {
+      ln_row_finish<LNK>(xln, d, eps, s_red, reinterpret_cast<uint2*>(s_x));
+    } else {
+      for (int b = 0; b < nb; ++b)
+        ln_row_f16<LNK>(reinterpret_cast<const float*>(x) + (size_t)b * d, d, eps, s_red,
+                        reinterpret_cast<uint2*>(s_x) + (size_t)b * d / 4);
+    }
     __syncthreads();
     if (blockIdx.x == 0) {
       const int n16 = nb * d / 8;  // d % 8 == 0
