@@ -50,6 +50,20 @@ __device__ __forceinline__ uint32_t q_chunk(const void* __restrict__ Q, const fl
   constexpr int ESZ = Tr<PT>::ESZ;
   __shared__ uint32_t s_mask[kBlock / kWave];
   const int lane = wave_lane(), wv = wave_id();
+  // h (all tokens, fp32, zero past r) goes through LDS once per workgroup: the four waves share it.
+  // Its loads go out before the Q rows (loads return in issue order), so the staging does not wait
+  // for the rows.
+  constexpr int HR = RV * kWave * EPL;  // h elements per token covered by the lanes' slices
+  constexpr int HPT = (NB * HR / 4 + kBlock - 1) / kBlock;  // float4 of h per thread
+  __shared__ float4 s_h[NB * HR / 4];
+  float4 hs[HPT];
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    const int k = threadIdx.x + u * kBlock;
+    const int b = k / (HR / 4), e = (k % (HR / 4)) * 4;  // r % 8 == 0: whole float4s
+    hs[u] = k < NB * HR / 4 && b < nb && e < r ? *reinterpret_cast<const float4*>(h + (size_t)b * r + e)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   uint4 qv[RPW][RV];
 #pragma unroll
   for (int k = 0; k < RPW; ++k)
@@ -58,12 +72,10 @@ __device__ __forceinline__ uint32_t q_chunk(const void* __restrict__ Q, const fl
       const int i = chunk_neuron<ILV, RPW>(q, NC, wv * RPW + k), e = v * kWave * EPL + lane * EPL;
       qv[k][v] = q_ld16z(reinterpret_cast<const char*>(Q) + ((size_t)i * r + e) * ESZ, i < F && i >= n_hot && e < r);
     }
-  // h (all tokens, fp32, zero past r) goes through LDS once per workgroup: the four waves share it
-  constexpr int HR = RV * kWave * EPL;  // h elements per token covered by the lanes' slices
-  __shared__ float4 s_h[NB * HR / 4];
-  for (int k = threadIdx.x; k < NB * HR / 4; k += kBlock) {
-    const int b = k / (HR / 4), e = (k % (HR / 4)) * 4;  // r % 8 == 0: whole float4s
-    s_h[k] = b < nb && e < r ? *reinterpret_cast<const float4*>(h + (size_t)b * r + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < HPT; ++u) {
+    const int k = threadIdx.x + u * kBlock;
+    if (k < NB * HR / 4) s_h[k] = hs[u];
   }
   __syncthreads();
   float hv[NB][RV][EPL];
