@@ -91,6 +91,20 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
   static_assert(LNK == 0 || kHThreads == kBlock, "ln_row_* take kBlock threads");
   float4 xln[(LNK > 0 && NB == 1) ? LNK : 1];
   if constexpr (LNK > 0 && NB == 1) ln_row_load<LNK>(reinterpret_cast<const float*>(x), d, xln);
+  // without the LayerNorm, x (all tokens) likewise goes out first when it is one round of 8 pieces
+  // of 16 bytes per thread
+  const int nx16 = (int)((size_t)nb * d * ESZ / 16);
+  const bool x1r = LNK == 0 && nx16 <= 8 * kHThreads;
+  uint4 xr8[LNK == 0 ? 8 : 1];
+  if constexpr (LNK == 0) {
+    if (x1r) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = threadIdx.x + u * kHThreads;
+        xr8[u] = k < nx16 ? reinterpret_cast<const uint4*>(x)[k] : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
   // this wave's row loads, then the workgroup stages x (all tokens) in LDS
   uint4 w[UN];
   int base = lane * EPL;
@@ -114,6 +128,13 @@ __global__ __launch_bounds__(kHThreads) void k_h(const void* __restrict__ A, con
       const int n16 = nb * d / 8;  // d % 8 == 0
       for (int k = threadIdx.x; k < n16; k += kHThreads) reinterpret_cast<uint4*>(hout)[k] = s_x[k];
     }
+  } else if (x1r) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int k = threadIdx.x + u * kHThreads;
+      if (k < nx16) s_x[k] = xr8[u];
+    }
+    __syncthreads();
   } else {
     stage_x<kHThreads>(x, (size_t)nb * d * ESZ, s_x);
   }
