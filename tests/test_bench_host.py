@@ -65,3 +65,28 @@ def test_traffic_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.measured_traffic("w", 1) is None
     first.write_text(code)
     assert bench.measured_traffic("w", 1) == 7
+
+
+def test_traffic_record_with_its_own_sources(tmp_path, monkeypatch):
+    # a record that names its own kernel sources is dropped by an edit to those files only
+    for f in bench.TRAFFIC_SOURCES + bench.BATCH_TRAFFIC_SOURCES:
+        p = tmp_path / f
+        p.parent.mkdir(parents=True, exist_ok=True)
+        p.write_text("int %s;\n" % p.stem)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    hb = bench.sources_hash(bench.BATCH_TRAFFIC_SOURCES)
+    monkeypatch.setattr(bench, "TRAFFIC", {("w", 8): {"files": bench.BATCH_TRAFFIC_SOURCES, "sources": hb, "bytes": 9}})
+    assert bench.measured_traffic("w", 8) == 9
+    only_b1 = [f for f in bench.TRAFFIC_SOURCES if f not in bench.BATCH_TRAFFIC_SOURCES][0]
+    (tmp_path / only_b1).write_text("int changed;\n")
+    assert bench.measured_traffic("w", 8) == 9
+    (tmp_path / bench.BATCH_TRAFFIC_SOURCES[-1]).write_text("int changed;\n")
+    assert bench.measured_traffic("w", 8) is None
+
+
+def test_layer_kernels_names_the_pipeline():
+    import synth
+    S = synth.CONFIGS
+    assert bench.layer_kernels(S["opt30b_relu_f16"], 1) == "k_h1, k_qu, k_dn"
+    assert bench.layer_kernels(S["opt175b_relu_i4"], 8).startswith("MFMA batch kernels: k_bh, k_bhred, k_bq_full, k_bscan")
+    assert "k_bup (orders the list)" in bench.layer_kernels(S["opt30b_relu_f16"], 4)
