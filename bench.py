@@ -373,7 +373,7 @@ def layer_kernels(spec, B, ln=False):
     if ln and B == 2 and spec.storage == "f16" and spec.act == "relu" and spec.r <= 1024:
         return "k_h with the LayerNorm, k_q, k_ud, k_reduce_ud"
     if ln and B > 1:
-        return "the LayerNorm kernel, then the small-batch or batch kernels by batch size"
+        return "the LayerNorm kernel, then " + layer_kernels(spec, B)
     if B == 1 and spec.storage == "f16" and spec.act == "relu" and spec.d <= 8192:
         return "k_h1, k_qu, k_dn"
     if B == 1 and spec.storage == "i4" and spec.act == "relu" and spec.d <= 16384:

@@ -90,3 +90,5 @@ def test_layer_kernels_names_the_pipeline():
     assert bench.layer_kernels(S["opt30b_relu_f16"], 1) == "k_h1, k_qu, k_dn"
     assert bench.layer_kernels(S["opt175b_relu_i4"], 8).startswith("MFMA batch kernels: k_bh, k_bhred, k_bq_full, k_bscan")
     assert "k_bup (orders the list)" in bench.layer_kernels(S["opt30b_relu_f16"], 4)
+    assert bench.layer_kernels(S["falcon40b_stack_f16"], 1, ln=True) == "k_h with the LayerNorm, k_qu, k_dn"
+    assert bench.layer_kernels(S["falcon40b_stack_f16"], 32, ln=True).startswith("the LayerNorm kernel, then MFMA batch kernels")
