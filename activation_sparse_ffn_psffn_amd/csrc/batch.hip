@@ -1375,7 +1375,7 @@ static void ffn_launch_nt(const BArgs& g, hipStream_t s, bool scan) {
   else ffn_launch_b<WT, ACT, 2>(g, s, scan);
 }
 
-// The layer call lets the up kernel order the list for fp16 weights (measured on MI355X, same box:
+// The layer call lets the up kernel order the list for fp16 weights (measured on MI355X, one machine:
 // OPT-30B shape at 4 tokens 60.3 -> 55.4 us, 48-layer stack at 4 and 32 tokens +2.5% and +1.4%
 // tokens/s); for 4-bit weights the larger LDS footprint of their 1024-element x chunk costs more
 // than the list kernel (OPT-175B shape at 8 tokens 107.2 -> 108.4 us), so they keep it.  The LDS

@@ -175,7 +175,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py: this build measures one GPU only (the path is a single-GPU decode step); "
+        log("bench.py: measures one GPU only (the path is a single-GPU decode step); "
             "--gpus %d is not supported" % args.gpus)
         sys.exit(2)
 

@@ -17,7 +17,7 @@ def test_graph_plan_covers_every_step_once(steps, graph_steps):
 
 
 def test_graph_plan_driver_command():
-    # the driver runs `bench.py --gpus 1 --steps 20 --warmup 5` with the default graph size
+    # `bench.py --gpus 1 --steps 20 --warmup 5` with the default graph size: one graph of 20 steps
     assert bench.graph_plan(20, 64) == [(0, 20)]
     assert bench.graph_plan(1024, 64) == [(64 * k, 64) for k in range(16)]
     assert bench.graph_plan(100, 64) == [(0, 64), (64, 36)]
