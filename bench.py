@@ -44,6 +44,10 @@ TRAFFIC = {
     ("opt30b_relu_f16", 1): {"sources": "f79e14099de5b787", "bytes": 101962137},
     # profiles/opt175b_relu_i4_b1_hbm_traffic.md: k_h1 + k_qu + k_dn (4-bit rows), 1.046x
     ("opt175b_relu_i4", 1): {"sources": "f79e14099de5b787", "bytes": 217172379},
+    # profiles/llama2_13b_swiglu_f16_b1_hbm_traffic.md: k_h + k_q + k_ud + k_reduce_ud, 1.040x
+    ("llama2_13b_swiglu_f16", 1): {"sources": "f79e14099de5b787", "bytes": 292533661},
+    # profiles/falcon40b_stack_f16_b1_hbm_traffic.md: per layer call, k_h with the LayerNorm + k_qu + k_dn, 1.035x
+    ("falcon40b_stack_f16", 1): {"sources": "f79e14099de5b787", "bytes": 157804407},
     # profiles/opt175b_relu_i4_b8_hbm_traffic.md: the eight batch kernels, 1.17x
     ("opt175b_relu_i4", 8): {"files": BATCH_TRAFFIC_SOURCES, "sources": "4381b58d6eb1cfba", "bytes": 318682435},
 }
@@ -445,7 +449,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
     exp_union = [float((1.0 - (1.0 - pl) ** B).sum()) for (_, _, pl) in layers]
     gbps = byt / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(spec.name, B),
             "kernel": "psffn_layer_ln (%s), 48 calls per step" % layer_kernels(spec, B, ln=True),
             "bytes_per_launch": int(byt / L), "avg_launch_us": round(ms * 1e3 / L, 3)}
     cpu = None
