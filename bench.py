@@ -113,6 +113,29 @@ def host_cpu():
     return n, model
 
 
+def device_copy_gbps(torch, mib=512, reps=5, trials=3):
+    """The GPU's measured copy bandwidth, as context for the fraction of the 8 TB/s nominal peak: a
+    device-to-device copy of `mib` MiB (read + written bytes) timed with events over `reps` copies,
+    the best of `trials` such batches."""
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    best = float("inf")
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record(st)
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) / reps)
+    del src, dst
+    return round(2 * n / (best * 1e-3) / 1e9, 1)
+
+
 def hot_prefix_len(counts, tokens, p_hot):
     """Length of the hot prefix of a hot-first layer (the neurons computed without prediction): the
     number of neurons whose profiled firing frequency counts[i] / tokens is at least p_hot.  counts
@@ -361,7 +384,8 @@ def main():
             if n_hot else ""), "batch": B, "d": spec.d, "F": spec.F, "r": spec.r, "n_hot": n_hot},
         "layer": {"gbps": round(layer_gbps, 1), "frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
                   "algorithmic_bytes_per_step": int(step_bytes), "mean_active": round(n_mean, 2),
-                  "tokens_per_s": round(1e6 / us_per_step * B, 1), "breakdown": breakdown},
+                  "tokens_per_s": round(1e6 / us_per_step * B, 1), "breakdown": breakdown,
+                  "device_copy_gbps": device_copy_gbps(torch)},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
@@ -462,6 +486,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
                                   "Zipf(1.0), residual + LayerNorm between layers" % (spec.name, L, d, F, spec.r, B),
                       "batch": B},
            "layer": {"us_per_layer": round(ms * 1e3 / L, 3), "gbps": round(gbps, 1),
+                     "device_copy_gbps": device_copy_gbps(torch),
                      "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                      "mean_union_active_per_layer": round(float(n.mean()), 1),
                      "union_active_per_layer_min_max": [int(n.min()), int(n.max())],
