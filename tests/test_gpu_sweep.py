@@ -1,0 +1,69 @@
+"""A seeded sweep of layer shapes against the oracle, beyond the fixed ragged cases: every storage
+type and activation, d from 8 (128 for 4-bit rows) to 2048, F from 1 to 3000 (fewer neurons than
+one chunk, one mask word, or one tile included), ranks 8 to 1600, batches 1 to 32 and densities
+from 2% to 50%.  Each case checks the logits and the active set against the oracle, the one-call
+layer against the predictor call followed by the FFN call (bit for bit), and y on the oracle's
+list against the oracle's sparse FFN.  The shapes are drawn once from a fixed seed."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import check_set, check_y, ffn_of, oracle_layer, pred_of, spec_variant, tol_for
+
+ps = pytest.importorskip("activation_sparse_ffn_psffn_amd")
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+BASE = {"f32": "tiny_relu_f32", "f16": "opt30b_relu_f16", "i4": "opt175b_relu_i4"}
+
+
+def draw_cases(n=64, seed=20261203):
+    rng = random.Random(seed)
+    out = []
+    for k in range(n):
+        st = rng.choice(["f32", "f16", "f16", "i4"])
+        act = rng.choice(["relu", "relu", "swiglu"])
+        d = 128 * rng.randint(1, 16) if st == "i4" else 8 * rng.randint(1, 256)
+        F = rng.choice([1, 2, 7, 15, 16, 17, 31, 33, 100, 257, 1000, 2049, 3000])
+        r = 8 * rng.randint(1, 200)
+        B = rng.choice([1, 1, 2, 3, 4, 5, 8, 16, 17, 31, 32])
+        dens = rng.choice([0.02, 0.1, 0.5])
+        out.append((k, st, act, d, F, r, B, dens))
+    return out
+
+
+@pytest.mark.parametrize("k,st,act,d,F,r,B,dens", draw_cases())
+def test_shape_sweep(k, st, act, d, F, r, B, dens):
+    print("sweep case %d: %s %s d=%d F=%d r=%d B=%d density %.2f" % (k, st, act, d, F, r, B, dens), flush=True)
+    spec = spec_variant(BASE[st], act=act, density=dens)
+    L = synth.make_layer(spec, seed=100 + k, device=DEV, d=d, F=F, r=r)
+    n = L.numpy()
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    X = synth.make_tokens(L.spec, B, seed=200 + k, device=DEV, d=d)
+    Xn = X.cpu().numpy()
+    logits = torch.empty(B, F, dtype=torch.float32, device=DEV)
+    idx, cnt = ps.predict(P, X, ws, logits=logits)
+    y1 = ps.sparse_ffn(W, X, idx, cnt, ws)
+    idx2, cnt2, y2 = ps.layer(P, W, X, ws)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    dl = np.abs(logits.cpu().numpy().astype(np.float64) - ref).max()
+    assert dl < 1e-5 * (1 + np.abs(ref).max()), "logits off by %.2e" % dl
+    stt = check_set(idx, cnt, ref)
+    m = int(cnt.item())
+    assert int(cnt2.item()) == m and torch.equal(idx2[:m], idx[:m]), "layer list differs from the predictor call"
+    assert torch.equal(y1, y2), "layer y differs from the two calls"
+    lst = oracle.compact(ref)
+    orc = oracle_layer(n, act)
+    y_o = ps.sparse_ffn(W, X, torch.from_numpy(lst).to(DEV) if len(lst) else torch.zeros(1, dtype=torch.int32, device=DEV),
+                        torch.tensor([len(lst)], dtype=torch.int32, device=DEV), ws)
+    torch.cuda.synchronize()
+    e = check_y(y_o.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for(st))
+    if stt["exact"]:
+        check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for(st))
+    print("  active %d of %d, max|dlogit| %.2e, rel err %.2e" % (m, F, dl, e), flush=True)
