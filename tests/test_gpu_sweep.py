@@ -67,3 +67,42 @@ def test_shape_sweep(k, st, act, d, F, r, B, dens):
     if stt["exact"]:
         check_y(y1.cpu().numpy(), orc.sparse_ffn(Xn, lst), tol_for(st))
     print("  active %d of %d, max|dlogit| %.2e, rel err %.2e" % (m, F, dl, e), flush=True)
+
+
+@pytest.mark.parametrize("k,st,act,d,F,r,B,dens", draw_cases()[:32])
+def test_shape_sweep_hot_prefix_and_stack_step(k, st, act, d, F, r, B, dens):
+    """The same shapes through the hot-prefix calls (a random prefix length: the prefix is listed
+    whatever its logits, the rest as the oracle's) and, with an fp16 predictor, the stack step
+    (psffn_layer_ln equals the LayerNorm kernel followed by the layer call, bit for bit)."""
+    rng = random.Random(7000 + k)
+    n_hot = rng.choice([1, F // 3, F])
+    print("sweep case %d (hot prefix %d, stack step): %s %s d=%d F=%d r=%d B=%d" % (k, n_hot, st, act, d, F, r, B),
+          flush=True)
+    spec = spec_variant(BASE[st], act=act, density=dens)
+    L = synth.make_layer(spec, seed=100 + k, device=DEV, d=d, F=F, r=r)
+    n = L.numpy()
+    W, P = ffn_of(L, ps), pred_of(L, ps)
+    ws = ps.new_workspace(P, W, B)
+    X = synth.make_tokens(L.spec, B, seed=200 + k, device=DEV, d=d)
+    Xn = X.cpu().numpy()
+    idx, cnt = ps.predict(P, X, ws, n_hot=n_hot)
+    y1 = ps.sparse_ffn(W, X, idx, cnt, ws)
+    idx2, cnt2, y2 = ps.layer(P, W, X, ws, n_hot=n_hot)
+    torch.cuda.synchronize()
+    ref = oracle.predict_logits(n["A"], n["Q"], n["c"], Xn)
+    check_set(idx, cnt, ref, n_hot=n_hot)
+    m = int(cnt.item())
+    assert int(cnt2.item()) == m and torch.equal(idx2[:m], idx[:m]) and torch.equal(y1, y2)
+    lst = oracle.compact(ref, n_hot=n_hot)
+    if m == len(lst) and np.array_equal(idx[:m].cpu().numpy(), lst):
+        check_y(y1.cpu().numpy(), oracle_layer(n, act).sparse_ffn(Xn, lst), tol_for(st))
+    if st == "f32":
+        return  # the stack step takes an fp16 predictor
+    x0 = synth.make_residual(L.spec, B, seed=300 + k, device=DEV, d=d)
+    x1 = x0.clone()
+    h1 = ps.layernorm_f16(x1)
+    ps.layer(P, W, h1, ws, y=x1, accumulate=True)
+    x2 = x0.clone()
+    _, _, h2 = ps.layer_ln(P, W, x2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2) and torch.equal(x1, x2), "layer_ln differs from LayerNorm + layer"
