@@ -1187,7 +1187,10 @@ static hipError_t layer_t(const psffn_predictor& P, const psffn_ffn& W, const vo
   const size_t xbytes = round256((size_t)B * P.d * Tr<PT>::ESZ);
   const int hgrid = (P.r + kHThreads / kWave - 1) / (kHThreads / kWave);
   if (xres == nullptr) {
-    k_h<PT, NB, 0><<<hgrid, kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h, 0.f, nullptr);
+    // one token, fp16: k_h1, as in the predictor call (the same h bits as k_h)
+    const hipError_t eh = PT == St::F16 && B == 1 ? launch_h1(P, x, h, s) : hipErrorNotSupported;
+    if (eh != hipSuccess && eh != hipErrorNotSupported) return eh;
+    if (eh == hipErrorNotSupported) k_h<PT, NB, 0><<<hgrid, kHThreads, xbytes, s>>>(P.A, x, P.d, P.r, B, h, 0.f, nullptr);
   } else {
     if constexpr (PT != St::F16) return hipErrorNotSupported;
     else {
