@@ -179,8 +179,10 @@ def main():
     ap.add_argument("--workload", default="opt30b_relu_f16")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=30,
-                    help="decode steps the CPU oracle baseline times (about 13 s of CPU work on the default layer)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle baseline: decode steps are timed until about this much CPU time is spent")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="CPU oracle baseline: at most this many decode steps (0: every token of the workload)")
     ap.add_argument("--no-events", action="store_true", help="skip the per-call event pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 8 times with a plain device copy and exit (reference "
@@ -371,7 +373,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, copies[0], X, B, args.cpu_tokens)
+        cpu = cpu_baseline(spec, copies[0], X, B, args.cpu_tokens, args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(us_per_step, 3), "unit": "us/layer", "n_gpus": 1, "steps": K,
@@ -478,7 +480,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
             "bytes_per_launch": int(byt / L), "avg_launch_us": round(ms * 1e3 / L, 3)}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_stack(spec, layers, x0, B, L)
+        cpu = cpu_baseline_stack(spec, layers, x0, B, L, budget_s=args.cpu_seconds)
     out = {"metric": "decode tokens/s through a stack of sparse FFN layers", "value": round(tok_s, 1),
            "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
@@ -759,9 +761,10 @@ def bench_study(args, spec, ps, synth, np, torch):
                       "rows": rows}), flush=True)
 
 
-def cpu_baseline(spec, copy0, X, B, ntok):
-    """The oracle (single-threaded fp64 C loops) timed on this host on `ntok` decode steps of the
-    same workload: predict, compact, sparse FFN over its own list."""
+def cpu_baseline(spec, copy0, X, B, max_steps, budget_s):
+    """The oracle (single-threaded fp64 C loops) timed on this host on decode steps of the same
+    workload (predict, compact, sparse FFN over its own list), one after another until about
+    `budget_s` seconds are spent, at most `max_steps` (0: every token) and at least one."""
     import numpy as np
 
     import oracle
@@ -771,11 +774,16 @@ def cpu_baseline(spec, copy0, X, B, ntok):
     A, Q, c = g(P.A), g(P.Q), g(P.c)
     lay = oracle.Layer(spec.act, g(W.w_up), g(W.w_dT), w_gate=g(W.w_gate), s_up=g(W.s_up), s_gate=g(W.s_gate),
                        s_dT=g(W.s_dT), b_up=g(W.b_up), b_gate=g(W.b_gate), b_down=g(W.b_down))
-    Xn = X[:ntok].cpu().numpy()
+    n = X.shape[0] if max_steps <= 0 else min(max_steps, X.shape[0])
+    Xn = X[:n].cpu().numpy()
     oracle.build()
     t0 = time.perf_counter()
-    for t in range(ntok):
-        oracle.predicted_layer(A, Q, c, lay, Xn[t])
+    ntok = 0
+    while ntok < n:
+        oracle.predicted_layer(A, Q, c, lay, Xn[ntok])
+        ntok += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
     log("cpu baseline: %d steps in %.2f s" % (ntok, dt))
     nproc, model = host_cpu()
