@@ -1,5 +1,6 @@
-"""Host logic of bench.py (no GPU): the partition of the timed steps into captured HIP graphs and
-the host CPU record of the oracle baseline."""
+"""Host logic of bench.py (no GPU): the partition of the timed steps into captured HIP graphs, the
+host CPU record and the step budget of the oracle baseline, the hot-prefix length, the traffic
+records and the kernel names of the roofline line."""
 import pytest
 
 import bench
@@ -92,3 +93,17 @@ def test_layer_kernels_names_the_pipeline():
     assert "k_bup (orders the list)" in bench.layer_kernels(S["opt30b_relu_f16"], 4)
     assert bench.layer_kernels(S["falcon40b_stack_f16"], 1, ln=True) == "k_h with the LayerNorm, k_qu, k_dn"
     assert bench.layer_kernels(S["falcon40b_stack_f16"], 32, ln=True).startswith("the LayerNorm kernel, then MFMA batch kernels")
+
+
+def test_cpu_baseline_budget_and_cap():
+    """The oracle baseline times decode steps until its CPU-time budget is spent (at least one),
+    at most the given number of steps (0: every token of the workload)."""
+    import synth
+
+    spec = synth.CONFIGS["tiny_relu_f32"]
+    L = synth.make_layer(spec, seed=1)
+    X = synth.make_tokens(spec, 6, seed=2).reshape(6, 1, spec.d)
+    r = bench.cpu_baseline(spec, (L, L), X, 1, 4, 100.0)
+    assert r["sample"].startswith("4 decode steps") and r["value"] > 0 and r["kind"] == "oracle"
+    assert bench.cpu_baseline(spec, (L, L), X, 1, 0, 0.0)["sample"].startswith("1 decode steps")
+    assert bench.cpu_baseline(spec, (L, L), X, 1, 0, 100.0)["sample"].startswith("6 decode steps")
