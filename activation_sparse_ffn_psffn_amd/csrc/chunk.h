@@ -15,8 +15,12 @@ namespace psffn {
 // read through this block when a lane has nothing to load, so every load stays unconditional
 static __device__ uint4 q_zero16[1] = {{0u, 0u, 0u, 0u}};  // never written
 
+// Q rows are read once per call: non-temporal loads, so that they do not push the reused lines (h,
+// the mask words, the kernels' code) out of L2; each load takes whole lines in one instruction
+typedef unsigned int q_u32x4v __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 q_ld16z(const void* p, bool ok) {
-  return *reinterpret_cast<const uint4*>(ok ? p : static_cast<const void*>(q_zero16));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                       reinterpret_cast<const q_u32x4v*>(ok ? p : static_cast<const void*>(q_zero16))));
 }
 
 // Chunk q of 4*RPW neurons, RPW per wave of a kBlock-thread workgroup.  ILV = 0 (contiguous): bit k
