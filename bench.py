@@ -79,6 +79,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# A bounded GPU spin queued right before a start event: the host then enqueues the event and the
+# timed graph replays while the GPU is still busy, so the events time the K steps on the GPU and not
+# the host's launch latency before the first of them (which a short run, such as 20 steps in one
+# graph, would otherwise spread over its steps).  About a millisecond at the shader clock.
+SPIN_CYCLES = 2_000_000
+
+
+def gpu_busy(torch):
+    torch.cuda._sleep(SPIN_CYCLES)
+
+
 def graph_plan(steps, graph_steps):
     """Partition of the K timed steps into consecutive captured HIP graphs: (first step, length)
     pairs covering [0, steps) in order.  Full graphs of graph_steps steps, then one shorter graph
@@ -126,6 +137,7 @@ def device_copy_gbps(torch, mib=512, reps=5, trials=3):
     best = float("inf")
     for _ in range(trials):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_busy(torch)
         e0.record(st)
         for _ in range(reps):
             dst.copy_(src)
@@ -304,6 +316,7 @@ def main():
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    gpu_busy(torch)
     e_start.record(stream)
     if graphs:
         for gr in graphs:
@@ -348,6 +361,7 @@ def main():
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         g_pred.replay()  # lists for the FFN replay, and warm
         torch.cuda.synchronize()
+        gpu_busy(torch)
         ev[0].record(stream)
         g_pred.replay()
         ev[1].record(stream)
@@ -462,6 +476,7 @@ def bench_stack(args, spec, ps, synth, np, torch):
     torch.cuda.synchronize()
     K = args.steps
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_busy(torch)
     e0.record(stream)
     for _ in range(K):
         g.replay()
@@ -662,6 +677,7 @@ def bench_sizing(args, spec, ps, synth, np, torch):
         torch.cuda.synchronize()
         K = max(1, min(args.steps, 64))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_busy(torch)
         e0.record(stream)
         for _ in range(K):
             g.replay()
@@ -745,6 +761,7 @@ def bench_study(args, spec, ps, synth, np, torch):
         gr.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gpu_busy(torch)
         e0.record()
         gr.replay()
         e1.record()
